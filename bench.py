@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark: paged decode attention on one GPU.
+
+One step = the step's copy-on-write copies (if any) + pa_kv_append +
+pa_decode (partition kernel, then merge kernel) for one layer of one workload,
+inputs resident in HBM.  Default workload: the OPT-13B layer (40 heads x 128,
+fp16, block 16, 30 sequences, contexts uniform in 128..2048).
+
+Timing (after the method of the "KV 缓存" topic page, level-3 script: inputs
+built outside the timed region, warm-up first, median with [min, max]):
+W untimed warm-up steps, then exactly K timed steps between device
+synchronisations, also split into 10 samples for median [min, max].  Steps
+rotate over several copies of the pool so consecutive steps do not find the
+previous step's K/V in the last-level cache.  Per-kernel durations come from
+HIP events the library records around its kernels on their own stream.
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "paged decode attention tokens/s and achieved HBM GB/s (% of peak), 1 GPU"
+
+
+def workload_label(wl):
+    return (f"{wl.name}: {wl.num_q_heads} q heads / {wl.num_kv_heads} kv heads x {wl.head_dim}, kv {wl.kv}, "
+            f"act {wl.act}, block {wl.block_size}, {wl.batch} seqs, ctx U[{wl.ctx_lo},{wl.ctx_hi}]"
+            + (f" after a shared {wl.prefix_len}-token prefix" if wl.prefix_len else ""))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_375_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, launch_bytes):
+    """HBM bytes per launch of the partition kernel from the committed counter
+    summary, or None when it is missing or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"decode_partition_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(dr, repeats):
+    """The CPU reference (plain scalar C, fp64, one thread) on the same step."""
+    from oracle.allocator import OracleAllocator
+    from oracle.reference_step import ReferenceStep
+    from paged_kv_cache_375_amd.workloads import run_scenario
+
+    ref = ReferenceStep(dr, run_scenario(dr, OracleAllocator(dr.num_blocks, dr.wl.block_size, dr.free_order)))
+    times = []
+    for _ in range(repeats):
+        t = time.perf_counter()
+        ref.append()
+        ref.decode()
+        times.append(time.perf_counter() - t)
+    med = statistics.median(times)
+    return {"value": dr.wl.batch / med, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole step (append + decode of all {dr.wl.batch} sequences, every head), "
+                      f"{repeats} runs, median {med:.2f} s [min {min(times):.2f}, max {max(times):.2f}]",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="opt13b")
+    ap.add_argument("--block-size", type=int, default=0, help="override the workload's block size")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--rotate", type=int, default=0, help="pool copies to rotate over (0: enough for >= 2 GB)")
+    ap.add_argument("--cpu-repeats", type=int, default=2, help="CPU reference runs (0 skips the CPU baseline)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM counters) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+        return
+
+    from paged_kv_cache_375_amd import api
+    from paged_kv_cache_375_amd.accounting import step_bytes, step_flops
+    from paged_kv_cache_375_amd.state import DecodeStep
+    from paged_kv_cache_375_amd.workloads import WORKLOADS, draw
+
+    wl = WORKLOADS[args.workload]
+    if args.block_size:
+        wl = wl.with_block_size(args.block_size)
+    print(f"bench: building {wl.name}", file=sys.stderr, flush=True)
+    dr = draw(wl, args.seed)
+    step = DecodeStep(dr, "cuda")
+    sc = step.scenario
+    sb = step_bytes(sc.ctx, sc.tables, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.act, wl.kv,
+                    len(sc.step_pairs))
+    pool_bytes = 2 * step.cache.k.numel() * step.cache.k.element_size()
+    rotate = args.rotate or max(1, min(8, math.ceil(2e9 / max(1, sb.kv_read_unique))))
+    caches = [step.cache] + [step.cache.with_pools(step.cache.k.clone(), step.cache.v.clone())
+                             for _ in range(rotate - 1)]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        step.run(caches[i % rotate])
+    torch.cuda.synchronize()
+
+    api.timing_enable(True)
+    api.timing_read()
+    K = args.steps
+    n_samples = 10 if K >= 10 else 1
+    per = K // n_samples
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_samples + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    evs[0].record(stream)
+    i = 0
+    for smp in range(n_samples):
+        n = per if smp < n_samples - 1 else K - per * (n_samples - 1)
+        for _ in range(n):
+            step.run(caches[i % rotate])
+            i += 1
+        evs[smp + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = evs[0].elapsed_time(evs[-1])
+    sample_ms = []
+    for smp in range(n_samples):
+        n = per if smp < n_samples - 1 else K - per * (n_samples - 1)
+        sample_ms.append(evs[smp].elapsed_time(evs[smp + 1]) / n)
+    part_ms, n_part, merge_ms, n_merge = api.timing_read()
+    api.timing_enable(False)
+
+    ms_per_step = total_ms / K
+    tokens_per_s = wl.batch / (ms_per_step / 1e3)
+    gbps = sb.total / (ms_per_step / 1e3) / 1e9
+    gbps_unique = sb.total_unique / (ms_per_step / 1e3) / 1e9
+    part_avg_ms = part_ms / max(1, n_part)
+    merge_avg_ms = merge_ms / max(1, n_merge)
+    # the partition kernel reads every cached K/V vector, q and the tables, and
+    # writes the output (or the partials the merge turns into it)
+    part_bytes = sb.kv_read_unique + sb.q_out + sb.tables
+    achieved = part_bytes / (part_avg_ms / 1e3) / 1e9
+    traffic = measured_traffic(wl.name, part_bytes)
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv if wl.kv != "e4m3" else "e4m3",
+        "accumulate": "f32",
+        "data": "synthetic (seeded normal K/V/q, uniform context lengths, shuffled block placement)",
+        "config": {
+            "workload": workload_label(wl),
+            "batch": wl.batch, "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim, "block_size": wl.block_size, "sum_ctx": int(sc.ctx.sum()),
+            "max_ctx": int(sc.ctx.max()), "cow_pairs": int(len(sc.step_pairs)), "seed": args.seed,
+            "layers": 1, "pool_bytes": pool_bytes, "pool_copies_rotated": rotate,
+        },
+        "step_bytes": {"total": sb.total, "kv_read": sb.kv_read, "kv_read_unique": sb.kv_read_unique,
+                       "append": sb.append, "q_out": sb.q_out, "tables": sb.tables, "cow": sb.cow},
+        "step_flops": step_flops(sc.ctx, wl.num_q_heads, wl.head_dim),
+        "gbps_step": gbps,
+        "gbps_step_unique": gbps_unique,
+        "hbm_frac_step": gbps_unique / HBM_PEAK_GBPS,
+        "samples_ms_per_step": {"median": statistics.median(sample_ms), "min": min(sample_ms),
+                                "max": max(sample_ms), "n": n_samples},
+        "kernels_ms": {"partition_avg": part_avg_ms, "partition_launches": n_part,
+                       "merge_avg": merge_avg_ms, "merge_launches": n_merge},
+        "wall_s_timed_region": wall,
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
+    }
+    if args.cpu_repeats > 0:
+        print("bench: timing the CPU reference", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(dr, args.cpu_repeats)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

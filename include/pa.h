@@ -1,0 +1,252 @@
+/*
+ * pa.h — paged KV-cache decode for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels and a host-side block allocator.
+ * All device entry points are asynchronous and stream-ordered; all host
+ * argument checks are synchronous and never read device memory.
+ *
+ * Citation key (web page title, then section):
+ *   [F55 §x]  "KV 缓存与分页注意力" (world.lapla.si, plate F55), section x
+ *   [AIF x]   "KV 缓存" (aiinfact.com topic page), part x
+ *   [IPX §x]  "读懂PagedAttention：vLLM的KV缓存与GPU显存管理" (iplexlaw.co.kr),
+ *             sub-heading x
+ *
+ * ---------------------------------------------------------------------------
+ * Memory layout of the pool (this library's choice; the pages only say that
+ * storing per layer and per head performs like storing all layers together
+ * [F55 §模型省略了什么]):
+ *
+ *   k_cache, v_cache: each [num_blocks][num_kv_heads][block_size][head_dim]
+ *   element (b, h, slot, i) at ((b * num_kv_heads + h) * block_size + slot)
+ *   * head_dim + i.  One (block, head) tile is contiguous.
+ *
+ * Block tables: int32 [num_seqs][max_blocks_per_seq], entry j = physical
+ * block of logical block j [F55 §块表].  Per-entry fill counts are implied by
+ * one context length per sequence: only the last block can be partial
+ * [F55 §块表], so entry j holds min(block_size, ctx - j * block_size) tokens.
+ * Unused entries may hold anything (conventionally -1).
+ *
+ * context_lens: int32 [num_seqs], tokens of each sequence INCLUDING the token
+ * appended in the current step (the new token attends to itself, because its
+ * K/V are appended before attention [AIF level-3 script]).
+ *
+ * Ownership: the caller owns every device buffer (pool, q, new K/V, output,
+ * tables, lengths, workspace) and the stream; the library allocates no device
+ * memory in these calls and keeps no device pointer between calls.  The
+ * allocator object is the only library-owned state.
+ *
+ * Supported shapes: head_dim in {32, 64, 128}; block_size a power of two in
+ * 1..64; num_q_heads a multiple of num_kv_heads; kv dtype f32, f16 or
+ * FP8 E4M3; activation dtype f32 or f16 (f32 only with an f32 pool).
+ * ---------------------------------------------------------------------------
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,
+  PA_ERR_OUT_OF_BLOCKS = 2,
+  PA_ERR_UNKNOWN_SEQ = 3,
+  PA_ERR_WORKSPACE_TOO_SMALL = 4,
+  PA_ERR_UNSUPPORTED = 5,
+  PA_ERR_HIP = 6
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
+
+/* Describes caller-owned device memory; the library keeps no pointer. */
+typedef struct {
+  void* k_cache;           /* device, [num_blocks][num_kv_heads][block_size][head_dim] */
+  void* v_cache;           /* device, same shape and dtype */
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t kv_dtype;        /* pa_dtype */
+  /* FP8 pools only: stored byte = e4m3_rne_saturate(f32(x) * inv_scale) with
+   * one binary32 multiply; value read back = e4m3 value * scale.  One scale
+   * per tensor (K and V separately).  Ignored for f32/f16 pools.  The pages
+   * say only that the cache may keep one byte per number [F55 §后来的做法]. */
+  float k_scale, v_scale, k_inv_scale, v_inv_scale;
+} pa_kv_cache;
+
+/* ============================ device operations ============================ */
+
+/*
+ * pa_kv_append — store the new token's K and V of every sequence into the
+ * free slot of its last block [F55 §一次写一个词元, §块表];
+ * [IPX §分离逻辑顺序与实际存储位置] (later tokens go into the last block's
+ * free slot).
+ *
+ *   pos = context_lens[s] - 1, blk = block_tables[s][pos / block_size],
+ *   k_cache[blk][h][pos % block_size][:] = k_new[s][h][:] for h < num_kv_heads
+ *   (same for V); FP8 pools quantise as described above.
+ *
+ * k_new, v_new: device, [num_seqs][num_kv_heads][head_dim] of dtype act.
+ * block_tables, context_lens: device (layouts above).  Sequences whose
+ * context length is < 1, whose position needs an entry past
+ * max_blocks_per_seq, or whose block id is outside [0, num_blocks) write
+ * nothing.  Precondition: no two sequences target the same (block, slot) —
+ * the allocator guarantees this by never letting a shared block be written
+ * (copy-on-write, pa_seq_append_slot + pa_copy_blocks).  Bit-exact for
+ * f32/f16 pools.  Re-running the call with the same arguments is idempotent.
+ */
+pa_status pa_kv_append(const pa_kv_cache* cache, const void* k_new, const void* v_new, int32_t act,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t max_blocks_per_seq, void* stream);
+
+/*
+ * pa_kv_write_prompt — the prompt phase: a sequence's whole prompt K/V are
+ * computed at once and stored into the blocks allocated for it
+ * [F55 §一次写一个词元]; [IPX §分离逻辑顺序与实际存储位置] (blocks for the input
+ * are allocated first).
+ *
+ * Sequence s stores token rows src_row[s] .. src_row[s] + count[s] - 1 of
+ * k_src / v_src ([total_rows][num_kv_heads][head_dim], dtype act) at logical
+ * positions start_pos[s] .. start_pos[s] + count[s] - 1, through its table.
+ * src_row: device int64 [num_seqs]; start_pos, count: device int32
+ * [num_seqs]; max_count >= every count[s] sizes the launch (tokens past
+ * max_count are not written).  Out-of-range positions or block ids write
+ * nothing.  Same precondition on distinct targets as pa_kv_append.
+ */
+pa_status pa_kv_write_prompt(const pa_kv_cache* cache, const void* k_src, const void* v_src, int32_t act,
+                             const int64_t* src_row, const int32_t* start_pos, const int32_t* count,
+                             const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                             int32_t max_count, void* stream);
+
+/*
+ * pa_copy_blocks — the copy of copy-on-write: before a sequence writes into
+ * a block other sequences still reference, the block is copied and the
+ * write goes to the copy [F55 §常见问题 (copy-on-write)];
+ * [IPX §同一提示生成两个回答的假想例子].
+ *
+ * src_dst_pairs: device int32 [n][2] = (source block, destination block);
+ * every KV head and slot of the block is copied, K and V.  Bit-exact.  Pairs
+ * with an id outside [0, num_blocks) are skipped.  Destinations must be
+ * distinct and no destination may be a source.
+ */
+pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst_pairs, int32_t n, void* stream);
+
+/*
+ * pa_decode_workspace_size — bytes of device workspace pa_decode needs for
+ * split-context partial results: fp32 (max, sum, vector) per (sequence,
+ * query head, partition).
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_context_len);
+
+/*
+ * pa_decode — one generation step's attention: for every sequence s and
+ * query head h, the query attends over all context_lens[s] cached keys and
+ * values of its KV head, fetched block by block through the block table
+ * (blocks need not be adjacent) in logical token order [F55 §块表];
+ * [IPX §分离逻辑顺序与实际存储位置].  Attention is the scaled dot-product
+ * softmax attention the pages cite, with the 1/sqrt(d) scale passed as
+ * sm_scale [AIF level-3 account table]:
+ *
+ *   s_t = sm_scale * q[s][h] . K_t,   out[s][h] = sum_t softmax(s)_t * V_t
+ *
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads) (grouped- and
+ * multi-query attention share one KV head among contiguous query heads
+ * [F55 §后来的做法]).  q, out: device [num_seqs][num_q_heads][head_dim] of
+ * dtype act; fp32 accumulation; the output is rounded to act (nearest even).
+ * Long contexts are split into partitions whose (max, sum, vector) partial
+ * results are merged exactly by a second kernel (the online softmax gives
+ * the same result [F55 related plate F51]).
+ *
+ * max_context_len must be >= every context_lens[s]; workspace must hold
+ * pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len)
+ * bytes (NULL allowed when that size is 0).  A context length of 0 yields
+ * zeros.  A sequence whose context exceeds max_context_len or
+ * max_blocks_per_seq * block_size, or whose table holds a block id outside
+ * [0, num_blocks), yields NaN for every head (and reads nothing out of range).
+ */
+pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* out, int32_t act, int32_t num_q_heads,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, float sm_scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ============================== host allocator ============================= */
+/*
+ * The block allocator keeps the bookkeeping of [F55 §像内存分页, §块表,
+ * §放不下的时候] and [IPX §同一提示生成两个回答的假想例子]:
+ *   - equal-size physical blocks in one pool, one table per sequence;
+ *   - a block is taken only when the sequence's earlier blocks are full;
+ *   - first come, first served, and a request is met whole or not at all
+ *     (a failing call changes nothing);
+ *   - a finished sequence returns its blocks;
+ *   - forks share blocks with reference counts; a write into a partially
+ *     filled block that others still reference copies it first.
+ * Free list: first in, first out (pop the head, freed blocks join the tail in
+ * logical order).  Not thread-safe: one owner at a time.  Sequence ids are
+ * any non-negative int32.
+ */
+typedef struct pa_allocator pa_allocator;
+
+typedef struct {
+  int32_t num_blocks;
+  int32_t num_free;
+  int32_t num_shared;       /* blocks with reference count > 1 */
+  int32_t num_seqs;
+  int64_t tokens_held;      /* distinct (block, slot) pairs holding a token */
+  int64_t slots_allocated;  /* blocks in use * block_size */
+} pa_allocator_stats;
+
+/* free_order: host int32 [num_blocks], a permutation giving the initial free
+ * list order (NULL = 0, 1, ..., num_blocks - 1). */
+pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                              pa_allocator** out);
+void pa_allocator_destroy(pa_allocator* a);
+int32_t pa_allocator_num_free(const pa_allocator* a);
+/* A new sequence holding num_tokens (>= 0) tokens: ceil(n / block_size) blocks. */
+pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens);
+/* child shares every block of parent (reference counts + 1). */
+pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child);
+/* Reserve the slot of one more token.  *cow_src / *cow_dst receive the block
+ * copy the caller must perform (pa_copy_blocks) before writing, or -1 / -1. */
+pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* cow_src, int32_t* cow_dst);
+/* Release the sequence: reference counts - 1, unreferenced blocks are freed. */
+pa_status pa_seq_free(pa_allocator* a, int32_t seq);
+/* Copy the table (up to cap entries) and report its length and context. */
+pa_status pa_seq_get(const pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
+                     int32_t* num_blocks, int32_t* context_len);
+/* Host int32 tables [n][max_blocks_per_seq] (padding -1) and lengths [n]. */
+pa_status pa_export_tables(const pa_allocator* a, const int32_t* seqs, int32_t n,
+                           int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out);
+int32_t pa_block_refcount(const pa_allocator* a, int32_t block);
+pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out);
+/* The sequence to preempt first when blocks run out: the latest arrival
+ * [F55 §放不下的时候]; -1 if none. */
+int32_t pa_latest_arrival(const pa_allocator* a);
+
+/* ================================ utilities ================================ */
+
+const char* pa_status_str(pa_status s);
+/* Detail of the last non-OK status returned on this thread (never NULL). */
+const char* pa_last_error(void);
+
+/*
+ * Kernel timing for measurement: while enabled, every pa_decode records HIP
+ * events around its partition kernel and its merge kernel, on the stream the
+ * kernels run on.  pa_timing_read synchronises those events and returns the
+ * summed milliseconds and the number of launches of each since the last
+ * read, then resets the sums.  Events are created on enable (up to 4096
+ * launches are kept) and destroyed on disable.  Not thread-safe.
+ */
+pa_status pa_timing_enable(int32_t on);
+pa_status pa_timing_read(double* partition_ms, int32_t* partition_launches,
+                         double* merge_ms, int32_t* merge_launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

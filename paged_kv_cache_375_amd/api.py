@@ -1,0 +1,223 @@
+"""Python face of the C ABI (same names, argument marshalling only).
+
+Device buffers are torch tensors; kernels run on torch's current HIP stream
+unless a stream is given.  Shapes and dtypes are checked here so that a
+mistake fails before any launch; the library checks again on its side.
+"""
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import PA_F16, PA_F32, PA_FP8_E4M3, PaAllocatorStats, PaKVCache, check, lib
+
+TORCH_DTYPE = {PA_F32: torch.float32, PA_F16: torch.float16, PA_FP8_E4M3: torch.uint8}
+DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.uint8: PA_FP8_E4M3}
+NAME_CODE = {"f32": PA_F32, "f16": PA_F16, "e4m3": PA_FP8_E4M3}
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+class KVCache:
+    """A K pool and a V pool, each [num_blocks][num_kv_heads][block_size][head_dim]."""
+
+    def __init__(self, num_blocks, block_size, num_kv_heads, head_dim, kv_dtype, device="cuda",
+                 k_scale=1.0, v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0, k=None, v=None):
+        kv_dtype = NAME_CODE.get(kv_dtype, kv_dtype)
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        tdt = TORCH_DTYPE[kv_dtype]
+        self.k = torch.zeros(shape, dtype=tdt, device=device) if k is None else _dev(k, tdt, "k", shape)
+        self.v = torch.zeros(shape, dtype=tdt, device=device) if v is None else _dev(v, tdt, "v", shape)
+        self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim = shape[0], block_size, num_kv_heads, head_dim
+        self.kv_dtype = kv_dtype
+        self.struct = PaKVCache(self.k.data_ptr(), self.v.data_ptr(), num_blocks, block_size, num_kv_heads, head_dim,
+                                kv_dtype, k_scale, v_scale, k_inv_scale, v_inv_scale)
+
+    def with_pools(self, k, v):
+        """The same description over another pair of pools of the same shape."""
+        s = self.struct
+        return KVCache(self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim, self.kv_dtype,
+                       k_scale=s.k_scale, v_scale=s.v_scale, k_inv_scale=s.k_inv_scale, v_inv_scale=s.v_inv_scale,
+                       k=k, v=v)
+
+
+def _act(t):
+    if t.dtype not in (torch.float32, torch.float16):
+        raise TypeError("activations must be float32 or float16")
+    return DTYPE_CODE[t.dtype]
+
+
+def kv_append(cache: KVCache, k_new, v_new, block_tables, context_lens, stream=None):
+    B = context_lens.shape[0]
+    act = _act(k_new)
+    shape = (B, cache.num_kv_heads, cache.head_dim)
+    _dev(k_new, k_new.dtype, "k_new", shape)
+    _dev(v_new, k_new.dtype, "v_new", shape)
+    _dev(block_tables, torch.int32, "block_tables")
+    _dev(context_lens, torch.int32, "context_lens", (B,))
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    check(lib().pa_kv_append(ctypes.byref(cache.struct), _ptr(k_new), _ptr(v_new), act, _ptr(block_tables),
+                             _ptr(context_lens), B, block_tables.shape[1], _stream(stream)))
+
+
+def kv_write_prompt(cache: KVCache, k_src, v_src, src_row, start_pos, count, block_tables, max_count, stream=None):
+    B = count.shape[0]
+    act = _act(k_src)
+    _dev(k_src, k_src.dtype, "k_src")
+    _dev(v_src, k_src.dtype, "v_src", k_src.shape)
+    if k_src.dim() != 3 or tuple(k_src.shape[1:]) != (cache.num_kv_heads, cache.head_dim):
+        raise ValueError("k_src must be [rows][num_kv_heads][head_dim]")
+    _dev(src_row, torch.int64, "src_row", (B,))
+    _dev(start_pos, torch.int32, "start_pos", (B,))
+    _dev(count, torch.int32, "count", (B,))
+    _dev(block_tables, torch.int32, "block_tables")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    check(lib().pa_kv_write_prompt(ctypes.byref(cache.struct), _ptr(k_src), _ptr(v_src), act, _ptr(src_row),
+                                   _ptr(start_pos), _ptr(count), _ptr(block_tables), B, block_tables.shape[1],
+                                   int(max_count), _stream(stream)))
+
+
+def copy_blocks(cache: KVCache, src_dst_pairs, stream=None):
+    _dev(src_dst_pairs, torch.int32, "src_dst_pairs")
+    if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise ValueError("src_dst_pairs must be [n][2]")
+    check(lib().pa_copy_blocks(ctypes.byref(cache.struct), _ptr(src_dst_pairs), src_dst_pairs.shape[0],
+                               _stream(stream)))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len):
+    return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len))
+
+
+def decode(cache: KVCache, q, block_tables, context_lens, max_context_len, sm_scale, out=None, workspace=None,
+           stream=None):
+    B, hq, d = q.shape
+    act = _act(q)
+    _dev(q, q.dtype, "q", (B, hq, cache.head_dim))
+    _dev(block_tables, torch.int32, "block_tables")
+    _dev(context_lens, torch.int32, "context_lens", (B,))
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, q.dtype, "out", q.shape)
+    need = decode_workspace_size(B, hq, d, max_context_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib().pa_decode(ctypes.byref(cache.struct), _ptr(q), _ptr(out), act, hq, _ptr(block_tables),
+                          _ptr(context_lens), B, block_tables.shape[1], int(max_context_len), float(sm_scale),
+                          _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def timing_enable(on=True):
+    check(lib().pa_timing_enable(1 if on else 0))
+
+
+def timing_read():
+    """(partition ms summed, partition launches, merge ms summed, merge launches) since the last read."""
+    pm, mm = ctypes.c_double(), ctypes.c_double()
+    pn, mn = ctypes.c_int32(), ctypes.c_int32()
+    check(lib().pa_timing_read(ctypes.byref(pm), ctypes.byref(pn), ctypes.byref(mm), ctypes.byref(mn)))
+    return pm.value, pn.value, mm.value, mn.value
+
+
+class OutOfBlocks(_lib.PagedAttnError):
+    pass
+
+
+class Allocator:
+    """The library's host block allocator (C++), with the same methods as the reference model."""
+
+    def __init__(self, num_blocks, block_size, free_order=None):
+        h = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise ValueError("free_order must have num_blocks entries")
+        check(lib().pa_allocator_create(num_blocks, block_size,
+                                        order.ctypes.data_as(ctypes.c_void_p) if order is not None else None,
+                                        ctypes.byref(h)))
+        self._h = h
+        self._order = order
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib().pa_allocator_destroy(h)
+            self._h = None
+
+    def _call(self, status):
+        if status == _lib.PA_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks(status, lib().pa_last_error().decode())
+        return check(status)
+
+    def num_free(self):
+        return lib().pa_allocator_num_free(self._h)
+
+    def allocate(self, seq, num_tokens):
+        self._call(lib().pa_seq_allocate(self._h, seq, num_tokens))
+
+    def fork(self, parent, child):
+        self._call(lib().pa_seq_fork(self._h, parent, child))
+
+    def append_slot(self, seq):
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        self._call(lib().pa_seq_append_slot(self._h, seq, ctypes.byref(src), ctypes.byref(dst)))
+        return (src.value, dst.value)
+
+    def free_seq(self, seq):
+        self._call(lib().pa_seq_free(self._h, seq))
+
+    def table(self, seq):
+        n, c = ctypes.c_int32(), ctypes.c_int32()
+        self._call(lib().pa_seq_get(self._h, seq, None, 0, ctypes.byref(n), ctypes.byref(c)))
+        buf = np.zeros(max(1, n.value), dtype=np.int32)
+        self._call(lib().pa_seq_get(self._h, seq, buf.ctypes.data_as(ctypes.c_void_p), n.value, ctypes.byref(n),
+                                    ctypes.byref(c)))
+        return buf[: n.value].tolist()
+
+    def export(self, seqs, max_blocks):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        t = np.zeros((len(seqs), max_blocks), dtype=np.int32)
+        c = np.zeros(len(seqs), dtype=np.int32)
+        self._call(lib().pa_export_tables(self._h, seqs.ctypes.data_as(ctypes.c_void_p), len(seqs), max_blocks,
+                                          t.ctypes.data_as(ctypes.c_void_p), c.ctypes.data_as(ctypes.c_void_p)))
+        return t, c
+
+    def refcount(self, block):
+        return lib().pa_block_refcount(self._h, block)
+
+    def stats(self):
+        s = PaAllocatorStats()
+        check(lib().pa_allocator_get_stats(self._h, ctypes.byref(s)))
+        return s
+
+    def latest_arrival(self):
+        r = lib().pa_latest_arrival(self._h)
+        return None if r < 0 else r

@@ -1,0 +1,220 @@
+// Host block allocator: the bookkeeping of paged KV storage.
+//
+// Rules (restated from [F55 §像内存分页, §块表, §放不下的时候, §常见问题] and
+// [IPX §分离逻辑顺序与实际存储位置, §同一提示生成两个回答的假想例子]):
+//   * one pool of equal blocks, one table of physical ids per sequence;
+//   * a block is taken only when the sequence's earlier blocks are full;
+//   * first come, first served; a request is met whole or not at all;
+//   * finished sequences return their blocks;
+//   * forks share blocks with reference counts; a write into a partially
+//     filled block another sequence still references copies it first, the
+//     original's count drops by one, full shared blocks stay shared.
+// The free list is first in, first out; blocks freed together join its tail
+// in logical order.  Every operation validates before it mutates, so a
+// failing call leaves the state unchanged.
+#include <algorithm>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "internal.h"
+
+struct pa_allocator {
+  struct Seq {
+    std::vector<int32_t> blocks;
+    int32_t ctx = 0;
+  };
+  int32_t num_blocks = 0;
+  int32_t block_size = 1;
+  std::deque<int32_t> free_list;
+  std::vector<int32_t> refcount;
+  std::unordered_map<int32_t, Seq> seqs;
+  std::vector<int32_t> arrival;  // first-come order of the live sequences
+
+  int32_t take() {
+    int32_t b = free_list.front();
+    free_list.pop_front();
+    refcount[b] = 1;
+    return b;
+  }
+};
+
+using pa::fail;
+using pa::ok;
+
+extern "C" pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                                         pa_allocator** out) {
+  if (!out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks < 0 || block_size < 1)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: num_blocks %d, block_size %d", num_blocks,
+                block_size);
+  pa_allocator* a = new (std::nothrow) pa_allocator;
+  if (!a) return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: out of host memory");
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->refcount.assign(num_blocks, 0);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete a;
+        return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: free_order is not a permutation (entry %d)", i);
+      }
+      seen[b] = 1;
+      a->free_list.push_back(b);
+    }
+  } else {
+    for (int32_t b = 0; b < num_blocks; ++b) a->free_list.push_back(b);
+  }
+  *out = a;
+  return ok();
+}
+
+extern "C" void pa_allocator_destroy(pa_allocator* a) { delete a; }
+
+extern "C" int32_t pa_allocator_num_free(const pa_allocator* a) {
+  return a ? static_cast<int32_t>(a->free_list.size()) : -1;
+}
+
+extern "C" pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens) {
+  if (!a || seq < 0 || num_tokens < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_allocate: bad argument (seq %d, tokens %d)", seq, num_tokens);
+  if (a->seqs.count(seq)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_allocate: sequence %d exists", seq);
+  int64_t need = (static_cast<int64_t>(num_tokens) + a->block_size - 1) / a->block_size;
+  if (need > static_cast<int64_t>(a->free_list.size()))
+    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_allocate: sequence %d needs %lld blocks, %zu free", seq,
+                static_cast<long long>(need), a->free_list.size());
+  pa_allocator::Seq s;
+  s.blocks.reserve(need);
+  for (int64_t i = 0; i < need; ++i) s.blocks.push_back(a->take());
+  s.ctx = num_tokens;
+  a->seqs.emplace(seq, std::move(s));
+  a->arrival.push_back(seq);
+  return ok();
+}
+
+extern "C" pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child) {
+  if (!a || child < 0) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_fork: bad argument");
+  auto it = a->seqs.find(parent);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_fork: unknown parent %d", parent);
+  if (a->seqs.count(child)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_fork: sequence %d exists", child);
+  pa_allocator::Seq s = it->second;
+  for (int32_t b : s.blocks) a->refcount[b] += 1;
+  a->seqs.emplace(child, std::move(s));
+  a->arrival.push_back(child);
+  return ok();
+}
+
+extern "C" pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* cow_src, int32_t* cow_dst) {
+  if (!a || !cow_src || !cow_dst) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_append_slot: NULL argument");
+  *cow_src = -1;
+  *cow_dst = -1;
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_append_slot: unknown sequence %d", seq);
+  pa_allocator::Seq& s = it->second;
+  if (s.ctx == INT32_MAX) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_append_slot: context overflow");
+  if (s.ctx % a->block_size == 0) {
+    // the last block is full (or there is none): lazily take a new one
+    if (a->free_list.empty())
+      return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_append_slot: no free block for sequence %d", seq);
+    s.blocks.push_back(a->take());
+  } else {
+    int32_t last = s.blocks.back();
+    if (a->refcount[last] > 1) {
+      // the slot lies in a partially filled block another sequence holds
+      if (a->free_list.empty())
+        return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_append_slot: no free block for the copy of block %d", last);
+      int32_t dst = a->take();
+      a->refcount[last] -= 1;
+      s.blocks.back() = dst;
+      *cow_src = last;
+      *cow_dst = dst;
+    }
+  }
+  s.ctx += 1;
+  return ok();
+}
+
+extern "C" pa_status pa_seq_free(pa_allocator* a, int32_t seq) {
+  if (!a) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_free: NULL allocator");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_free: unknown sequence %d", seq);
+  for (int32_t b : it->second.blocks) {
+    a->refcount[b] -= 1;
+    if (a->refcount[b] == 0) a->free_list.push_back(b);
+  }
+  a->seqs.erase(it);
+  a->arrival.erase(std::find(a->arrival.begin(), a->arrival.end(), seq));
+  return ok();
+}
+
+extern "C" pa_status pa_seq_get(const pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
+                                int32_t* num_blocks, int32_t* context_len) {
+  if (!a || cap < 0 || (cap > 0 && !block_ids)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_get: bad argument");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_get: unknown sequence %d", seq);
+  const auto& s = it->second;
+  int32_t n = static_cast<int32_t>(s.blocks.size());
+  for (int32_t i = 0; i < n && i < cap; ++i) block_ids[i] = s.blocks[i];
+  if (num_blocks) *num_blocks = n;
+  if (context_len) *context_len = s.ctx;
+  return ok();
+}
+
+extern "C" pa_status pa_export_tables(const pa_allocator* a, const int32_t* seqs, int32_t n,
+                                      int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out) {
+  if (!a || n < 0 || max_blocks_per_seq < 0 || (n > 0 && (!seqs || !tables_out || !context_lens_out)))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_export_tables: bad argument");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seqs[i]);
+    if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_export_tables: unknown sequence %d", seqs[i]);
+    if (static_cast<int64_t>(it->second.blocks.size()) > max_blocks_per_seq)
+      return fail(PA_ERR_INVALID_ARGUMENT, "pa_export_tables: sequence %d holds %zu blocks > %d", seqs[i],
+                  it->second.blocks.size(), max_blocks_per_seq);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& s = a->seqs.find(seqs[i])->second;
+    int32_t* row = tables_out + static_cast<size_t>(i) * max_blocks_per_seq;
+    int32_t j = 0;
+    for (; j < static_cast<int32_t>(s.blocks.size()); ++j) row[j] = s.blocks[j];
+    for (; j < max_blocks_per_seq; ++j) row[j] = -1;
+    context_lens_out[i] = s.ctx;
+  }
+  return ok();
+}
+
+extern "C" int32_t pa_block_refcount(const pa_allocator* a, int32_t block) {
+  if (!a || block < 0 || block >= a->num_blocks) return -1;
+  return a->refcount[block];
+}
+
+extern "C" pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out) {
+  if (!a || !out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_get_stats: NULL argument");
+  out->num_blocks = a->num_blocks;
+  out->num_free = static_cast<int32_t>(a->free_list.size());
+  out->num_shared = 0;
+  for (int32_t c : a->refcount) out->num_shared += (c > 1);
+  out->num_seqs = static_cast<int32_t>(a->seqs.size());
+  // a slot holds a token when some sequence's context covers it; count each
+  // physical (block, slot) once, so shared prefixes are not double counted
+  std::vector<int32_t> filled(a->num_blocks, 0);
+  for (const auto& kv : a->seqs) {
+    const auto& s = kv.second;
+    for (size_t j = 0; j < s.blocks.size(); ++j) {
+      int64_t f = std::min<int64_t>(a->block_size, static_cast<int64_t>(s.ctx) - static_cast<int64_t>(j) * a->block_size);
+      filled[s.blocks[j]] = std::max<int32_t>(filled[s.blocks[j]], static_cast<int32_t>(f));
+    }
+  }
+  out->tokens_held = 0;
+  for (int32_t f : filled) out->tokens_held += f;
+  out->slots_allocated = static_cast<int64_t>(a->num_blocks - out->num_free) * a->block_size;
+  return ok();
+}
+
+extern "C" int32_t pa_latest_arrival(const pa_allocator* a) {
+  if (!a || a->arrival.empty()) return -1;
+  return a->arrival.back();
+}

@@ -1,0 +1,220 @@
+// The C ABI of the device operations: host-side argument checks (never
+// reading device memory), dispatch to the kernels, and kernel timing.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "internal.h"
+#include "launch.h"
+
+using pa::fail;
+using pa::ok;
+
+namespace {
+
+constexpr int kMaxGridYZ = 65535;
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+pa_status check_cache(const pa_kv_cache* c, const char* fn) {
+  if (!c) return fail(PA_ERR_INVALID_ARGUMENT, "%s: cache is NULL", fn);
+  if (!c->k_cache || !c->v_cache) return fail(PA_ERR_INVALID_ARGUMENT, "%s: k_cache/v_cache is NULL", fn);
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_blocks %d, num_kv_heads %d", fn, c->num_blocks, c->num_kv_heads);
+  if (!is_pow2(c->block_size) || c->block_size > 64)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d is not a power of two in 1..64", fn, c->block_size);
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {32, 64, 128}", fn, c->head_dim);
+  if (c->kv_dtype != PA_F32 && c->kv_dtype != PA_F16 && c->kv_dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: kv_dtype %d", fn, c->kv_dtype);
+  if (c->kv_dtype == PA_FP8_E4M3 &&
+      !(c->k_scale > 0.f && c->v_scale > 0.f && c->k_inv_scale > 0.f && c->v_inv_scale > 0.f))
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: FP8 scales must be positive", fn);
+  return PA_OK;
+}
+
+pa_status check_act(const pa_kv_cache* c, int32_t act, const char* fn) {
+  const bool okpair = (act == PA_F32 && (c->kv_dtype == PA_F32 || c->kv_dtype == PA_FP8_E4M3)) ||
+                      (act == PA_F16 && (c->kv_dtype == PA_F16 || c->kv_dtype == PA_FP8_E4M3));
+  if (!okpair) return fail(PA_ERR_UNSUPPORTED, "%s: activation dtype %d with pool dtype %d", fn, act, c->kv_dtype);
+  return PA_OK;
+}
+
+pa_status hip_status(hipError_t e, const char* fn) {
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+int32_t max_parts_for(int32_t max_context_len) {
+  return max_context_len <= 0 ? 1 : (max_context_len + pa::kPartitionTokens - 1) / pa::kPartitionTokens;
+}
+
+// ---- kernel timing ----------------------------------------------------------
+constexpr int kTimingSlots = 4096;
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> part_ev, merge_ev;  // start/stop pairs
+  int n_part = 0, n_merge = 0;
+};
+Timing g_timing;
+
+void timing_release() {
+  for (hipEvent_t e : g_timing.part_ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : g_timing.merge_ev) (void)hipEventDestroy(e);
+  g_timing = Timing();
+}
+
+}  // namespace
+
+extern "C" pa_status pa_kv_append(const pa_kv_cache* cache, const void* k_new, const void* v_new, int32_t act,
+                                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t max_blocks_per_seq, void* stream) {
+  static const char* fn = "pa_kv_append";
+  if (pa_status s = check_cache(cache, fn)) return s;
+  if (pa_status s = check_act(cache, act, fn)) return s;
+  if (num_seqs < 0 || max_blocks_per_seq < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+  if (num_seqs > 0 && (!k_new || !v_new || !block_tables || !context_lens))
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL device pointer", fn);
+  return hip_status(pa::launch_append(*cache, k_new, v_new, act, block_tables, context_lens, num_seqs,
+                                      max_blocks_per_seq, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+extern "C" pa_status pa_kv_write_prompt(const pa_kv_cache* cache, const void* k_src, const void* v_src, int32_t act,
+                                        const int64_t* src_row, const int32_t* start_pos, const int32_t* count,
+                                        const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                        int32_t max_count, void* stream) {
+  static const char* fn = "pa_kv_write_prompt";
+  if (pa_status s = check_cache(cache, fn)) return s;
+  if (pa_status s = check_act(cache, act, fn)) return s;
+  if (num_seqs < 0 || max_blocks_per_seq < 0 || max_count < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+  if (num_seqs > kMaxGridYZ) return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs %d > %d", fn, num_seqs, kMaxGridYZ);
+  if (num_seqs > 0 && max_count > 0 && (!k_src || !v_src || !src_row || !start_pos || !count || !block_tables))
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL device pointer", fn);
+  return hip_status(pa::launch_write_prompt(*cache, k_src, v_src, act, src_row, start_pos, count, block_tables,
+                                            num_seqs, max_blocks_per_seq, max_count,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+extern "C" pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst_pairs, int32_t n,
+                                    void* stream) {
+  static const char* fn = "pa_copy_blocks";
+  if (pa_status s = check_cache(cache, fn)) return s;
+  if (n < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: negative pair count", fn);
+  if (n > kMaxGridYZ) return fail(PA_ERR_UNSUPPORTED, "%s: %d pairs > %d per call", fn, n, kMaxGridYZ);
+  if (n > 0 && !src_dst_pairs) return fail(PA_ERR_INVALID_ARGUMENT, "%s: pairs is NULL", fn);
+  return hip_status(pa::launch_copy_blocks(*cache, src_dst_pairs, n, static_cast<hipStream_t>(stream)), fn);
+}
+
+extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                           int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const int32_t parts = max_parts_for(max_context_len);
+  if (parts <= 1) return 0;
+  return static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+}
+
+extern "C" pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* out, int32_t act, int32_t num_q_heads,
+                               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t max_context_len, float sm_scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  static const char* fn = "pa_decode";
+  if (pa_status s = check_cache(cache, fn)) return s;
+  if (pa_status s = check_act(cache, act, fn)) return s;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: bad size (seqs %d, q heads %d, max blocks %d, max ctx %d)", fn,
+                num_seqs, num_q_heads, max_blocks_per_seq, max_context_len);
+  if (num_q_heads % cache->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", fn, num_q_heads,
+                cache->num_kv_heads);
+  if (num_seqs > kMaxGridYZ || num_q_heads > kMaxGridYZ)
+    return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs %d / num_q_heads %d above %d", fn, num_seqs, num_q_heads,
+                kMaxGridYZ);
+  if (!(sm_scale == sm_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: sm_scale is NaN", fn);
+  if (num_seqs == 0) return ok();
+  if (!q || !out || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL device pointer", fn);
+  const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, cache->head_dim, max_context_len);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
+
+  pa::DecodeArgs a{};
+  a.cache = cache;
+  a.q = q;
+  a.out = out;
+  a.act = act;
+  a.num_q_heads = num_q_heads;
+  a.tables = block_tables;
+  a.ctx = context_lens;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.max_parts = max_parts_for(max_context_len);
+  a.sm_scale = sm_scale;
+  float* ws = static_cast<float*>(workspace);
+  a.ws_ml = need > 0 ? ws : nullptr;
+  a.ws_o = need > 0 ? ws + static_cast<size_t>(num_seqs) * num_q_heads * a.max_parts * 2 : nullptr;
+  a.stream = static_cast<hipStream_t>(stream);
+  const bool timed = g_timing.on && g_timing.n_part < kTimingSlots && g_timing.n_merge < kTimingSlots;
+  if (timed) {
+    a.ev[0] = g_timing.part_ev[2 * g_timing.n_part];
+    a.ev[1] = g_timing.part_ev[2 * g_timing.n_part + 1];
+    a.ev[2] = g_timing.merge_ev[2 * g_timing.n_merge];
+    a.ev[3] = g_timing.merge_ev[2 * g_timing.n_merge + 1];
+  }
+  bool merged = false;
+  const hipError_t e = pa::launch_decode(a, &merged);
+  if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "%s: unsupported dtype/shape combination", fn);
+  if (timed && e == hipSuccess) {
+    g_timing.n_part += 1;
+    g_timing.n_merge += merged ? 1 : 0;
+  }
+  return hip_status(e, fn);
+}
+
+extern "C" pa_status pa_timing_enable(int32_t on) {
+  timing_release();
+  if (!on) return ok();
+  g_timing.part_ev.resize(2 * kTimingSlots);
+  g_timing.merge_ev.resize(2 * kTimingSlots);
+  for (auto* v : {&g_timing.part_ev, &g_timing.merge_ev}) {
+    for (hipEvent_t& e : *v) {
+      hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) {
+        e = nullptr;
+        timing_release();
+        return fail(PA_ERR_HIP, "pa_timing_enable: %s", hipGetErrorString(r));
+      }
+    }
+  }
+  g_timing.on = true;
+  return ok();
+}
+
+extern "C" pa_status pa_timing_read(double* partition_ms, int32_t* partition_launches, double* merge_ms,
+                                    int32_t* merge_launches) {
+  if (!partition_ms || !partition_launches || !merge_ms || !merge_launches)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_timing_read: NULL argument");
+  *partition_ms = *merge_ms = 0.0;
+  *partition_launches = g_timing.n_part;
+  *merge_launches = g_timing.n_merge;
+  for (int i = 0; i < g_timing.n_part; ++i) {
+    float ms = 0.f;
+    hipError_t r = hipEventSynchronize(g_timing.part_ev[2 * i + 1]);
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.part_ev[2 * i], g_timing.part_ev[2 * i + 1]);
+    if (r != hipSuccess) return fail(PA_ERR_HIP, "pa_timing_read: %s", hipGetErrorString(r));
+    *partition_ms += ms;
+  }
+  for (int i = 0; i < g_timing.n_merge; ++i) {
+    float ms = 0.f;
+    hipError_t r = hipEventSynchronize(g_timing.merge_ev[2 * i + 1]);
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.merge_ev[2 * i], g_timing.merge_ev[2 * i + 1]);
+    if (r != hipSuccess) return fail(PA_ERR_HIP, "pa_timing_read: %s", hipGetErrorString(r));
+    *merge_ms += ms;
+  }
+  g_timing.n_part = g_timing.n_merge = 0;
+  return ok();
+}

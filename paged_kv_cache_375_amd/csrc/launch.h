@@ -1,0 +1,43 @@
+// Host-side launchers of the HIP kernels (defined in the .hip files).
+#pragma once
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "pa.h"
+
+namespace pa {
+
+// Tokens per split-context partition of the decode kernels.
+constexpr int kPartitionTokens = 256;
+
+hipError_t launch_append(const pa_kv_cache& c, const void* k_new, const void* v_new, int act, const int32_t* tables,
+                         const int32_t* ctx, int num_seqs, int max_blocks, hipStream_t st);
+hipError_t launch_write_prompt(const pa_kv_cache& c, const void* k_src, const void* v_src, int act,
+                               const int64_t* src_row, const int32_t* start_pos, const int32_t* count,
+                               const int32_t* tables, int num_seqs, int max_blocks, int max_count, hipStream_t st);
+hipError_t launch_copy_blocks(const pa_kv_cache& c, const int32_t* pairs, int n, hipStream_t st);
+
+struct DecodeArgs {
+  const pa_kv_cache* cache;
+  const void* q;
+  void* out;
+  int act;
+  int num_q_heads;
+  const int32_t* tables;
+  const int32_t* ctx;
+  int num_seqs;
+  int max_blocks;
+  int max_ctx;
+  int max_parts;  // partitions the workspace holds per (sequence, head)
+  float sm_scale;
+  float* ws_ml;   // [num_seqs][num_q_heads][max_parts][2]: running max (log2 units), sum
+  float* ws_o;    // [num_seqs][num_q_heads][max_parts][head_dim]: unnormalised output
+  hipStream_t stream;
+  hipEvent_t ev[4];  // optional timing events: partition start/stop, merge start/stop (or null)
+};
+
+// Returns hipErrorInvalidValue for an unsupported dtype/shape combination.
+hipError_t launch_decode(const DecodeArgs& a, bool* merge_launched);
+
+}  // namespace pa

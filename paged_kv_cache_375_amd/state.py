@@ -1,0 +1,64 @@
+"""Device state of one decode step, built from a workload draw.
+
+Input construction (untimed): the library's allocator lays out the block
+tables (``workloads.run_scenario``), the history is written into the pool by
+the library's prompt-write kernel (prefix first, then the copy-on-write
+copies made while sequences grew, then each sequence's own tokens).
+
+``DecodeStep.run()`` is one step of the hot path: the step's copy-on-write
+copies (if any), the append of every sequence's new K/V, and the decode.
+"""
+import math
+
+import numpy as np
+import torch
+
+from . import api
+from .workloads import Draw, run_scenario
+
+
+def _to(a, device):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DecodeStep:
+    def __init__(self, dr: Draw, device="cuda", scenario=None):
+        wl = dr.wl
+        self.draw = dr
+        if scenario is None:
+            scenario = run_scenario(dr, api.Allocator(dr.num_blocks, wl.block_size, dr.free_order))
+        self.scenario = sc = scenario
+        self.device = device
+        self.cache = api.KVCache(dr.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim, wl.kv, device,
+                                 dr.k_scale, dr.v_scale, dr.k_inv_scale, dr.v_inv_scale)
+        k_hist, v_hist = _to(dr.k_hist, device), _to(dr.v_hist, device)
+        P = wl.prefix_len
+        if P:
+            one = lambda v, dt: torch.tensor([v], dtype=dt, device=device)
+            api.kv_write_prompt(self.cache, k_hist, v_hist, one(0, torch.int64), one(0, torch.int32),
+                                one(P, torch.int32), _to(sc.prefix_table, device), P)
+            if len(sc.hist_pairs):
+                api.copy_blocks(self.cache, _to(sc.hist_pairs, device))
+        if k_hist.shape[0] > P:
+            api.kv_write_prompt(self.cache, k_hist, v_hist, _to(dr.hist_row, device), _to(dr.hist_start, device),
+                                _to(dr.hist_count, device), _to(sc.hist_tables, device), int(dr.hist_count.max()))
+        del k_hist, v_hist
+        self.q = _to(dr.q, device)
+        self.k_new = _to(dr.k_new, device)
+        self.v_new = _to(dr.v_new, device)
+        self.tables = _to(sc.tables, device)
+        self.ctx = _to(sc.ctx, device)
+        self.step_pairs = _to(sc.step_pairs, device) if len(sc.step_pairs) else None
+        self.max_ctx = int(sc.ctx.max())
+        self.sm_scale = float(np.float32(1.0 / math.sqrt(wl.head_dim)))
+        self.out = torch.empty_like(self.q)
+        need = api.decode_workspace_size(wl.batch, wl.num_q_heads, wl.head_dim, self.max_ctx)
+        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+    def run(self, cache=None, stream=None):
+        c = cache or self.cache
+        if self.step_pairs is not None:
+            api.copy_blocks(c, self.step_pairs, stream)
+        api.kv_append(c, self.k_new, self.v_new, self.tables, self.ctx, stream)
+        api.decode(c, self.q, self.tables, self.ctx, self.max_ctx, self.sm_scale, self.out, self.workspace, stream)
+        return self.out
