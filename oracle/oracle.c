@@ -89,12 +89,13 @@ static double round_half_even(double q) {
 }
 
 /* binary32 -> E4M3, round to nearest even, saturating: finite magnitudes and
- * infinities beyond the largest code become +-448 (code 0x7E), NaN becomes
- * 0x7F with the input's sign. */
+ * infinities beyond the largest code become +-448 (code 0x7E).  Every NaN
+ * becomes 0x7F: IEEE 754 does not give the sign of a NaN any meaning (an
+ * arithmetic result's NaN sign is unspecified), so the store does not keep it. */
 uint8_t oracle_e4m3_encode(float y) {
   uint8_t sign = signbit(y) ? 0x80 : 0x00;
   double a = fabs((double)y);
-  if (isnan(y)) return (uint8_t)(sign | 0x7f);
+  if (isnan(y)) return (uint8_t)0x7f;
   if (a > 448.0) return (uint8_t)(sign | 0x7e);
   if (a < ldexp(1.0, -6)) {
     /* subnormal range: value = m * 2^-9, m = 0..8 (8 is the least normal) */
