@@ -64,11 +64,17 @@ __device__ __forceinline__ float e4m3_clamp(float x) {
 }
 
 // Four floats -> four E4M3 bytes (little-endian order a, b, c, d), rounded to
-// nearest even by the hardware conversion after saturation.
+// nearest even by the hardware conversion after saturation.  Every NaN is
+// stored as 0x7F whatever its sign (a NaN's sign carries no meaning).
 __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), v, true);
-  return static_cast<uint32_t>(v);
+  uint32_t r = static_cast<uint32_t>(v);
+  r = (a != a) ? ((r & 0xFFFFFF00u) | 0x0000007Fu) : r;
+  r = (b != b) ? ((r & 0xFFFF00FFu) | 0x00007F00u) : r;
+  r = (c != c) ? ((r & 0xFF00FFFFu) | 0x007F0000u) : r;
+  r = (d != d) ? ((r & 0x00FFFFFFu) | 0x7F000000u) : r;
+  return r;
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -59,7 +59,9 @@ def test_fp8_store_exhaustive_over_f16_inputs():
         want = kp.reshape(-1)
         finite = np.isfinite(x.reshape(-1))
         bad = np.nonzero(got != want)[0]
-        print(f"[fp8] scale {scale}: {len(bad)} mismatches ({np.sum(~finite[bad])} non-finite inputs)", flush=True)
+        print(f"[fp8] scale {scale}: {len(bad)} mismatches ({np.sum(~finite[bad])} non-finite inputs); first: "
+              f"{[(hex(int(x.reshape(-1).view(np.uint16)[i])), int(got[i]), int(want[i])) for i in bad[:4]]}",
+              flush=True)
         assert np.array_equal(got[finite], want[finite])
         assert np.array_equal(got, want)
 
