@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark: paged decode attention on one GPU.
 
-One step = the step's copy-on-write copies (if any) + pa_kv_append +
-pa_decode (partition kernel, then merge kernel) for one layer of one workload,
-inputs resident in HBM.  Default workload: the OPT-13B layer (40 heads x 128,
+One step = the step's copy-on-write copies (if any) + the append of every
+sequence's new K/V + the decode attention, for one layer of one workload,
+inputs resident in HBM; append and decode run as one launch (pa_decode_step).  Default workload: the OPT-13B layer (40 heads x 128,
 fp16, block 16, 30 sequences, contexts uniform in 128..2048).
 
 Timing (after the method of the "KV 缓存" topic page, level-3 script: inputs
@@ -49,9 +49,9 @@ def kernel_source_hash():
 
 
 def measured_traffic(workload, launch_bytes):
-    """HBM bytes per launch of the partition kernel from the committed counter
+    """HBM bytes per launch of the decode kernel from the committed counter
     summary, or None when it is missing or the kernels changed since."""
-    path = os.path.join(ROOT, "profiles", f"decode_partition_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -160,7 +160,7 @@ def main():
     for smp in range(n_samples):
         n = per if smp < n_samples - 1 else K - per * (n_samples - 1)
         sample_ms.append(evs[smp].elapsed_time(evs[smp + 1]) / n)
-    part_ms, n_part, merge_ms, n_merge = api.timing_read()
+    part_ms, n_part = api.timing_read()
     api.timing_enable(False)
 
     ms_per_step = total_ms / K
@@ -168,10 +168,10 @@ def main():
     gbps = sb.total / (ms_per_step / 1e3) / 1e9
     gbps_unique = sb.total_unique / (ms_per_step / 1e3) / 1e9
     part_avg_ms = part_ms / max(1, n_part)
-    merge_avg_ms = merge_ms / max(1, n_merge)
-    # the partition kernel reads every cached K/V vector, q and the tables, and
-    # writes the output (or the partials the merge turns into it)
-    part_bytes = sb.kv_read_unique + sb.q_out + sb.tables
+    # the decode kernel appends the new K/V (read from the caller, written into
+    # the pool), reads every cached K/V vector once, q and the tables, and
+    # writes the output; copy-on-write copies are a separate launch
+    part_bytes = sb.total_unique - sb.cow
     achieved = part_bytes / (part_avg_ms / 1e3) / 1e9
     traffic = measured_traffic(wl.name, part_bytes)
 
@@ -204,10 +204,10 @@ def main():
         "hbm_frac_step": gbps_unique / HBM_PEAK_GBPS,
         "samples_ms_per_step": {"median": statistics.median(sample_ms), "min": min(sample_ms),
                                 "max": max(sample_ms), "n": n_samples},
-        "kernels_ms": {"partition_avg": part_avg_ms, "partition_launches": n_part,
-                       "merge_avg": merge_avg_ms, "merge_launches": n_merge},
+        "kernels_ms": {"decode_avg": part_avg_ms, "decode_launches": n_part},
         "wall_s_timed_region": wall,
-        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel (append + split-context attention + merge)",
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
     }

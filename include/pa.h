@@ -136,9 +136,11 @@ pa_status pa_kv_write_prompt(const pa_kv_cache* cache, const void* k_src, const 
 pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst_pairs, int32_t n, void* stream);
 
 /*
- * pa_decode_workspace_size — bytes of device workspace pa_decode needs for
- * split-context partial results: fp32 (max, sum, vector) per (sequence,
- * query head, partition).
+ * pa_decode_workspace_size — bytes of device workspace pa_decode and
+ * pa_decode_step need for split-context partial results: an int32 arrival
+ * counter per (sequence, query head), padded to 256 bytes, then fp32
+ * (max, sum) and an unnormalised vector per (sequence, query head,
+ * partition).  0 when every context fits one partition (512 tokens).
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t max_context_len);
@@ -158,14 +160,22 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  * multi-query attention share one KV head among contiguous query heads
  * [F55 §后来的做法]).  q, out: device [num_seqs][num_q_heads][head_dim] of
  * dtype act; fp32 accumulation; the output is rounded to act (nearest even).
- * Long contexts are split into partitions whose (max, sum, vector) partial
- * results are merged exactly by a second kernel (the online softmax gives
- * the same result [F55 related plate F51]).
+ * Contexts longer than one 512-token partition are split; each partition's
+ * (max, sum, vector) partial result is merged exactly, in the same launch,
+ * by the last partition of that (sequence, head) to finish (the online
+ * softmax gives the same result [F55 related plate F51]).
  *
  * max_context_len must be >= every context_lens[s]; workspace must hold
  * pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len)
- * bytes (NULL allowed when that size is 0).  A context length of 0 yields
- * zeros.  A sequence whose context exceeds max_context_len or
+ * bytes (NULL allowed when that size is 0).  The workspace must be
+ * zero-filled before its first use: its arrival counters (the first
+ * num_seqs * num_q_heads int32, padded to 256 bytes) must start at zero, and
+ * every completed call leaves them at zero again, so a workspace can be
+ * reused call after call with the same num_seqs and num_q_heads (any
+ * max_context_len it is large enough for); calls with other sizes need a
+ * workspace zero-filled for them.  Calls that overlap in time must not share
+ * a workspace.  A context length of 0 yields zeros.  A
+ * sequence whose context exceeds max_context_len or
  * max_blocks_per_seq * block_size, or whose table holds a block id outside
  * [0, num_blocks), yields NaN for every head (and reads nothing out of range).
  */
@@ -173,6 +183,23 @@ pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* out, int32_t 
                     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                     int32_t max_blocks_per_seq, int32_t max_context_len, float sm_scale,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_step — the whole generation step in one launch: the result of
+ * pa_kv_append(cache, k_new, v_new, ...) followed by pa_decode(...) with the
+ * same arguments — the new token's K/V are stored into the free slot of the
+ * last block [F55 §一次写一个词元, §块表] and attended to — without a second
+ * pass over memory: the workgroups that hold the new token take it from
+ * k_new/v_new directly, and one of them stores it.  Same arguments, layouts,
+ * workspace contract and error behaviour as the two calls; the pool ends
+ * bit-identical to what pa_kv_append writes.  Copy-on-write copies
+ * (pa_copy_blocks) must be issued before it on the same stream.
+ */
+pa_status pa_decode_step(const pa_kv_cache* cache, const void* q, const void* k_new, const void* v_new,
+                         void* out, int32_t act, int32_t num_q_heads, const int32_t* block_tables,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* ============================== host allocator ============================= */
 /*
@@ -234,16 +261,15 @@ const char* pa_status_str(pa_status s);
 const char* pa_last_error(void);
 
 /*
- * Kernel timing for measurement: while enabled, every pa_decode records HIP
- * events around its partition kernel and its merge kernel, on the stream the
- * kernels run on.  pa_timing_read synchronises those events and returns the
- * summed milliseconds and the number of launches of each since the last
- * read, then resets the sums.  Events are created on enable (up to 4096
- * launches are kept) and destroyed on disable.  Not thread-safe.
+ * Kernel timing for measurement: while enabled, every pa_decode and
+ * pa_decode_step records HIP events around its kernel, on the stream the
+ * kernel runs on.  pa_timing_read synchronises those events and returns the
+ * summed milliseconds and the number of launches since the last read, then
+ * resets the sums.  Events are created on enable (up to 4096 launches are
+ * kept between reads) and destroyed on disable.  Not thread-safe.
  */
 pa_status pa_timing_enable(int32_t on);
-pa_status pa_timing_read(double* partition_ms, int32_t* partition_launches,
-                         double* merge_ms, int32_t* merge_launches);
+pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches);
 
 #ifdef __cplusplus
 }

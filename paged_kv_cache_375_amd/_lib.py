@@ -16,7 +16,7 @@ PA_F32, PA_F16, PA_FP8_E4M3 = 0, 1, 2
 
 # every symbol the public header declares
 EXPORTS = (
-    "pa_kv_append", "pa_kv_write_prompt", "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode",
+    "pa_kv_append", "pa_kv_write_prompt", "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode", "pa_decode_step",
     "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free", "pa_seq_allocate", "pa_seq_fork",
     "pa_seq_append_slot", "pa_seq_free", "pa_seq_get", "pa_export_tables", "pa_block_refcount",
     "pa_allocator_get_stats", "pa_latest_arrival", "pa_status_str", "pa_last_error", "pa_timing_enable",
@@ -66,6 +66,8 @@ def lib():
         "pa_copy_blocks": (st, [P(PaKVCache), vp, i32, vp]),
         "pa_decode_workspace_size": (ctypes.c_size_t, [i32, i32, i32, i32]),
         "pa_decode": (st, [P(PaKVCache), vp, vp, i32, i32, vp, vp, i32, i32, i32, f32, vp, ctypes.c_size_t, vp]),
+        "pa_decode_step": (st, [P(PaKVCache), vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, f32, vp,
+                                ctypes.c_size_t, vp]),
         "pa_allocator_create": (st, [i32, i32, vp, P(vp)]),
         "pa_allocator_destroy": (None, [vp]),
         "pa_allocator_num_free": (i32, [vp]),
@@ -81,7 +83,7 @@ def lib():
         "pa_status_str": (ctypes.c_char_p, [st]),
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_timing_enable": (st, [i32]),
-        "pa_timing_read": (st, [P(ctypes.c_double), P(i32), P(ctypes.c_double), P(i32)]),
+        "pa_timing_read": (st, [P(ctypes.c_double), P(i32)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

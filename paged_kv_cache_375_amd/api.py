@@ -111,10 +111,14 @@ def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len):
     return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len))
 
 
-def decode(cache: KVCache, q, block_tables, context_lens, max_context_len, sm_scale, out=None, workspace=None,
-           stream=None):
+def new_workspace(num_seqs, num_q_heads, head_dim, max_context_len, device="cuda"):
+    """A zero-filled decode workspace (its arrival counters must start at zero)."""
+    need = decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len)
+    return torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+
+
+def _decode_args(cache, q, block_tables, context_lens, max_context_len, out, workspace):
     B, hq, d = q.shape
-    act = _act(q)
     _dev(q, q.dtype, "q", (B, hq, cache.head_dim))
     _dev(block_tables, torch.int32, "block_tables")
     _dev(context_lens, torch.int32, "context_lens", (B,))
@@ -123,13 +127,36 @@ def decode(cache: KVCache, q, block_tables, context_lens, max_context_len, sm_sc
     if out is None:
         out = torch.empty_like(q)
     _dev(out, q.dtype, "out", q.shape)
-    need = decode_workspace_size(B, hq, d, max_context_len)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if workspace is None:
+        workspace = new_workspace(B, hq, d, max_context_len, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    return out, workspace, ws_bytes
+
+
+def decode(cache: KVCache, q, block_tables, context_lens, max_context_len, sm_scale, out=None, workspace=None,
+           stream=None):
+    """Attention of every sequence's query over its paged context (pa_decode)."""
+    B, hq, d = q.shape
+    act = _act(q)
+    out, workspace, ws_bytes = _decode_args(cache, q, block_tables, context_lens, max_context_len, out, workspace)
     check(lib().pa_decode(ctypes.byref(cache.struct), _ptr(q), _ptr(out), act, hq, _ptr(block_tables),
                           _ptr(context_lens), B, block_tables.shape[1], int(max_context_len), float(sm_scale),
                           _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def decode_step(cache: KVCache, q, k_new, v_new, block_tables, context_lens, max_context_len, sm_scale, out=None,
+                workspace=None, stream=None):
+    """Append of the new K/V and decode in one launch (pa_decode_step)."""
+    B, hq, d = q.shape
+    act = _act(q)
+    shape = (B, cache.num_kv_heads, cache.head_dim)
+    _dev(k_new, q.dtype, "k_new", shape)
+    _dev(v_new, q.dtype, "v_new", shape)
+    out, workspace, ws_bytes = _decode_args(cache, q, block_tables, context_lens, max_context_len, out, workspace)
+    check(lib().pa_decode_step(ctypes.byref(cache.struct), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), act, hq,
+                               _ptr(block_tables), _ptr(context_lens), B, block_tables.shape[1],
+                               int(max_context_len), float(sm_scale), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 
@@ -138,11 +165,10 @@ def timing_enable(on=True):
 
 
 def timing_read():
-    """(partition ms summed, partition launches, merge ms summed, merge launches) since the last read."""
-    pm, mm = ctypes.c_double(), ctypes.c_double()
-    pn, mn = ctypes.c_int32(), ctypes.c_int32()
-    check(lib().pa_timing_read(ctypes.byref(pm), ctypes.byref(pn), ctypes.byref(mm), ctypes.byref(mn)))
-    return pm.value, pn.value, mm.value, mn.value
+    """(decode kernel ms summed, launches) since the last read."""
+    ms, n = ctypes.c_double(), ctypes.c_int32()
+    check(lib().pa_timing_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 class OutOfBlocks(_lib.PagedAttnError):

@@ -54,14 +54,13 @@ int32_t max_parts_for(int32_t max_context_len) {
 constexpr int kTimingSlots = 4096;
 struct Timing {
   bool on = false;
-  std::vector<hipEvent_t> part_ev, merge_ev;  // start/stop pairs
-  int n_part = 0, n_merge = 0;
+  std::vector<hipEvent_t> part_ev;  // start/stop pairs around each decode kernel
+  int n_part = 0;
 };
 Timing g_timing;
 
 void timing_release() {
   for (hipEvent_t e : g_timing.part_ev) (void)hipEventDestroy(e);
-  for (hipEvent_t e : g_timing.merge_ev) (void)hipEventDestroy(e);
   g_timing = Timing();
 }
 
@@ -109,19 +108,29 @@ extern "C" pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src
   return hip_status(pa::launch_copy_blocks(*cache, src_dst_pairs, n, static_cast<hipStream_t>(stream)), fn);
 }
 
+// Workspace: arrival counters [num_seqs][num_q_heads] int32 (padded to 256
+// bytes), then (max, sum) pairs and unnormalised vectors per partition.
+static size_t counters_bytes(int32_t num_seqs, int32_t num_q_heads) {
+  const size_t b = static_cast<size_t>(num_seqs) * num_q_heads * sizeof(int32_t);
+  return (b + 255) & ~static_cast<size_t>(255);
+}
+
 extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                            int32_t max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
   const int32_t parts = max_parts_for(max_context_len);
   if (parts <= 1) return 0;
-  return static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+  return counters_bytes(num_seqs, num_q_heads) +
+         static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
 }
 
-extern "C" pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* out, int32_t act, int32_t num_q_heads,
-                               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                               int32_t max_blocks_per_seq, int32_t max_context_len, float sm_scale, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-  static const char* fn = "pa_decode";
+namespace {
+
+pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q, const void* k_new, const void* v_new,
+                        void* out, int32_t act, int32_t num_q_heads, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (pa_status s = check_cache(cache, fn)) return s;
   if (pa_status s = check_act(cache, act, fn)) return s;
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
@@ -135,7 +144,7 @@ extern "C" pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* ou
                 kMaxGridYZ);
   if (!(sm_scale == sm_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: sm_scale is NaN", fn);
   if (num_seqs == 0) return ok();
-  if (!q || !out || !block_tables || !context_lens)
+  if (!q || !out || !block_tables || !context_lens || (k_new == nullptr) != (v_new == nullptr))
     return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL device pointer", fn);
   const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, cache->head_dim, max_context_len);
   if (workspace_bytes < need || (need > 0 && !workspace))
@@ -145,6 +154,8 @@ extern "C" pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* ou
   a.cache = cache;
   a.q = q;
   a.out = out;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.act = act;
   a.num_q_heads = num_q_heads;
   a.tables = block_tables;
@@ -154,67 +165,72 @@ extern "C" pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* ou
   a.max_ctx = max_context_len;
   a.max_parts = max_parts_for(max_context_len);
   a.sm_scale = sm_scale;
-  float* ws = static_cast<float*>(workspace);
-  a.ws_ml = need > 0 ? ws : nullptr;
-  a.ws_o = need > 0 ? ws + static_cast<size_t>(num_seqs) * num_q_heads * a.max_parts * 2 : nullptr;
+  if (need > 0) {
+    char* base = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<int*>(base);
+    a.ws_ml = reinterpret_cast<float*>(base + counters_bytes(num_seqs, num_q_heads));
+    a.ws_o = a.ws_ml + static_cast<size_t>(num_seqs) * num_q_heads * a.max_parts * 2;
+  }
   a.stream = static_cast<hipStream_t>(stream);
-  const bool timed = g_timing.on && g_timing.n_part < kTimingSlots && g_timing.n_merge < kTimingSlots;
+  const bool timed = g_timing.on && g_timing.n_part < kTimingSlots;
   if (timed) {
     a.ev[0] = g_timing.part_ev[2 * g_timing.n_part];
     a.ev[1] = g_timing.part_ev[2 * g_timing.n_part + 1];
-    a.ev[2] = g_timing.merge_ev[2 * g_timing.n_merge];
-    a.ev[3] = g_timing.merge_ev[2 * g_timing.n_merge + 1];
   }
-  bool merged = false;
-  const hipError_t e = pa::launch_decode(a, &merged);
+  const hipError_t e = pa::launch_decode(a);
   if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "%s: unsupported dtype/shape combination", fn);
-  if (timed && e == hipSuccess) {
-    g_timing.n_part += 1;
-    g_timing.n_merge += merged ? 1 : 0;
-  }
+  if (timed && e == hipSuccess) g_timing.n_part += 1;
   return hip_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* out, int32_t act, int32_t num_q_heads,
+                               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t max_context_len, float sm_scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return decode_common("pa_decode", cache, q, nullptr, nullptr, out, act, num_q_heads, block_tables, context_lens,
+                       num_seqs, max_blocks_per_seq, max_context_len, sm_scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_decode_step(const pa_kv_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                    void* out, int32_t act, int32_t num_q_heads, const int32_t* block_tables,
+                                    const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                    int32_t max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_step: k_new/v_new is NULL");
+  return decode_common("pa_decode_step", cache, q, k_new, v_new, out, act, num_q_heads, block_tables, context_lens,
+                       num_seqs, max_blocks_per_seq, max_context_len, sm_scale, workspace, workspace_bytes, stream);
 }
 
 extern "C" pa_status pa_timing_enable(int32_t on) {
   timing_release();
   if (!on) return ok();
   g_timing.part_ev.resize(2 * kTimingSlots);
-  g_timing.merge_ev.resize(2 * kTimingSlots);
-  for (auto* v : {&g_timing.part_ev, &g_timing.merge_ev}) {
-    for (hipEvent_t& e : *v) {
-      hipError_t r = hipEventCreate(&e);
-      if (r != hipSuccess) {
-        e = nullptr;
-        timing_release();
-        return fail(PA_ERR_HIP, "pa_timing_enable: %s", hipGetErrorString(r));
-      }
+  for (hipEvent_t& e : g_timing.part_ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      timing_release();
+      return fail(PA_ERR_HIP, "pa_timing_enable: %s", hipGetErrorString(r));
     }
   }
   g_timing.on = true;
   return ok();
 }
 
-extern "C" pa_status pa_timing_read(double* partition_ms, int32_t* partition_launches, double* merge_ms,
-                                    int32_t* merge_launches) {
-  if (!partition_ms || !partition_launches || !merge_ms || !merge_launches)
-    return fail(PA_ERR_INVALID_ARGUMENT, "pa_timing_read: NULL argument");
-  *partition_ms = *merge_ms = 0.0;
-  *partition_launches = g_timing.n_part;
-  *merge_launches = g_timing.n_merge;
+extern "C" pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches) {
+  if (!decode_ms || !decode_launches) return fail(PA_ERR_INVALID_ARGUMENT, "pa_timing_read: NULL argument");
+  *decode_ms = 0.0;
+  *decode_launches = g_timing.n_part;
   for (int i = 0; i < g_timing.n_part; ++i) {
     float ms = 0.f;
     hipError_t r = hipEventSynchronize(g_timing.part_ev[2 * i + 1]);
     if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.part_ev[2 * i], g_timing.part_ev[2 * i + 1]);
     if (r != hipSuccess) return fail(PA_ERR_HIP, "pa_timing_read: %s", hipGetErrorString(r));
-    *partition_ms += ms;
+    *decode_ms += ms;
   }
-  for (int i = 0; i < g_timing.n_merge; ++i) {
-    float ms = 0.f;
-    hipError_t r = hipEventSynchronize(g_timing.merge_ev[2 * i + 1]);
-    if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_timing.merge_ev[2 * i], g_timing.merge_ev[2 * i + 1]);
-    if (r != hipSuccess) return fail(PA_ERR_HIP, "pa_timing_read: %s", hipGetErrorString(r));
-    *merge_ms += ms;
-  }
-  g_timing.n_part = g_timing.n_merge = 0;
+  g_timing.n_part = 0;
   return ok();
 }

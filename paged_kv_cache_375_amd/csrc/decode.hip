@@ -1,18 +1,28 @@
-// Paged decode attention: split-context partition kernel + merge kernel.
+// Paged decode attention in one launch: split-context partitions, an exact
+// merge by the last partition to finish, and optionally the append of the
+// step's new token.
 //
 // One workgroup per (partition of kPartitionTokens tokens, query head,
-// sequence).  It stages the partition's slice of the block table in LDS,
-// then every wavefront streams K/V rows with 16-byte loads: a token's
+// sequence).  Every wavefront streams K/V rows with 16-byte loads: a token's
 // head_dim numbers are spread over LPT consecutive lanes (16 bytes each), so
-// one wave load covers TPL = 64 / LPT tokens.  The lane's partial q.k is
-// summed across its LPT lanes, each lane keeps a running (max, sum, vector)
-// online softmax for the tokens of its row [F55 related plate F51: the
-// compute-as-you-go softmax gives the same result], and rows, wavefronts and
-// finally partitions are merged with the same exact rescaling.  Scores are
-// kept in log2 units (scaled by sm_scale * log2(e)) so exp2 is used.
+// one wave load covers TPL = 64 / LPT tokens, and the NW waves of the
+// workgroup cover ROUND = NW * TPL consecutive tokens per round.  The lane's
+// partial q.k is summed across its LPT lanes with DPP row operations, each
+// lane keeps a running (max, sum, vector) online softmax for the tokens of
+// its row [F55 related plate F51: the compute-as-you-go softmax gives the
+// same result], and rows, wavefronts and finally partitions are merged with
+// the same exact rescaling.  Scores are kept in log2 units (scaled by
+// sm_scale * log2(e)) so exp2 is used.
 //
 // Blocks are fetched through the table in logical token order; physical
 // blocks need not be adjacent [F55 §块表]; [IPX §分离逻辑顺序与实际存储位置].
+// When a block holds at least TPL tokens, the TPL tokens of one wave load
+// always lie in one block, so the block id is wave-uniform: the partition's
+// table slice is loaded once into registers (one entry per lane) and read
+// with readlane; smaller blocks stage the slice in LDS and look it up per
+// lane.  Loads are never
+// predicated: lanes past the context re-read the last token (a cache hit)
+// and their scores are masked to -inf.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -25,7 +35,44 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Per-dtype arithmetic on one lane's 16-byte K or V chunk.
+// Launch shape: wavefronts per workgroup and wave loads per batch.
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 4
+#endif
+#ifndef PA_DECODE_UNROLL
+#define PA_DECODE_UNROLL 8
+#endif
+// Grid order: 1 = query head varies fastest (the K/V tiles of neighbouring
+// heads of one block are adjacent in the pool), 0 = partition fastest.
+#ifndef PA_GRID_HEAD_FIRST
+#define PA_GRID_HEAD_FIRST 1
+#endif
+
+// ---- cross-lane sums -------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over aligned groups of N lanes; every lane of a group gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<kQuadXor1>(v);
+  if constexpr (N >= 4) v += dpp<kQuadXor2>(v);
+  if constexpr (N >= 8) v += dpp<kRowHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp<kRowMirror>(v);
+  if constexpr (N >= 32) v += __shfl_xor(v, 16);
+  if constexpr (N >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ---- per-dtype arithmetic on one lane's 16-byte K or V chunk ---------------
+
 template <typename KV, typename ACT>
 struct Math;
 
@@ -111,10 +158,14 @@ struct Math<fp8_t, ACT> {  // E4M3 pool: exact hardware conversion to f32
   }
 };
 
-template <typename KV>
-struct KVBytes {
-  static constexpr int value = Elem<KV>::bytes;
-};
+// Device-coherent (agent scope) accesses for data exchanged between
+// workgroups of one launch, which may run on different XCDs.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Merge (m, l, acc) with another state: exact rescaling to the larger max.
 template <int EPL>
@@ -128,95 +179,190 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   m = mn;
 }
 
-template <typename KV, typename ACT, int D, int NW, int U>
-__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
-    const char* __restrict__ kc, const char* __restrict__ vc, const ACT* __restrict__ q, ACT* __restrict__ out,
-    const int32_t* __restrict__ tables, const int32_t* __restrict__ ctx_lens, float* __restrict__ ws_ml,
-    float* __restrict__ ws_o, int num_blocks, int log2_bs, int hkv, int hq, int group, int max_blocks, int max_ctx,
-    int max_parts, float score_scale, float v_scale) {
+// The new token's 16-byte chunk c in pool format (quantised for FP8 pools),
+// read from a [head_dim] row of activations.
+template <typename KV, typename ACT>
+struct NewChunk;
+template <typename T>
+struct NewChunk<T, T> {
+  static __device__ __forceinline__ Vec16 load(const char* row, int c, float) { return load16(row + c * 16); }
+};
+template <>
+struct NewChunk<fp8_t, half_t> {  // 16 numbers = 32 bytes of f16
+  static __device__ __forceinline__ Vec16 load(const char* row, int c, float inv) {
+    const uint2 a = f16x8_to_e4m3(load16(row + c * 32), inv), b = f16x8_to_e4m3(load16(row + c * 32 + 16), inv);
+    return Vec16{{a.x, a.y, b.x, b.y}};
+  }
+};
+template <>
+struct NewChunk<fp8_t, float> {  // 16 numbers = 64 bytes of f32
+  static __device__ __forceinline__ Vec16 load(const char* row, int c, float inv) {
+    Vec16 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = f32x4_chunk_to_e4m3(load16(row + c * 64 + 16 * i), inv);
+    return r;
+  }
+};
+
+struct Params {
+  const char* kc;  // K pool
+  const char* vc;  // V pool
+  char* kw;        // the same pools, written by the fused append
+  char* vw;
+  const void* q;
+  void* out;
+  const char* k_new;  // [num_seqs][hkv][D] activations, or null (no append)
+  const char* v_new;
+  const int32_t* tables;
+  const int32_t* ctx;
+  int* counters;  // [num_seqs][hq] partition arrival counts (zero between calls)
+  float* ws_ml;   // [num_seqs][hq][max_parts][2]
+  float* ws_o;    // [num_seqs][hq][max_parts][D]
+  int num_blocks, log2_bs, hkv, hq, group, max_blocks, max_ctx, max_parts;
+  float score_scale, v_scale, k_inv, v_inv;
+};
+
+// BIG: block_size >= TPL (block id wave-uniform, table slice in registers).
+template <typename KV, typename ACT, int D, int NW, int U, bool BIG>
+__global__ __launch_bounds__(NW * 64) void decode_kernel(const Params P) {
   using M = Math<KV, ACT>;
   constexpr int EPL = M::EPL;
   constexpr int LPT = D / EPL;
   constexpr int TPL = 64 / LPT;
   constexpr int PART = kPartitionTokens;
   constexpr int ROUND = NW * TPL;
+  constexpr int KVB = Elem<KV>::bytes;
   static_assert(LPT >= 1 && LPT <= 64 && 64 % LPT == 0, "head_dim does not fit the lane layout");
 
-  const int p = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int p = PA_GRID_HEAD_FIRST ? blockIdx.y : blockIdx.x;
+  const int h = PA_GRID_HEAD_FIRST ? blockIdx.x : blockIdx.y;
+  const int s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = lane / LPT, c = lane % LPT;
+  const int log2_bs = P.log2_bs;
   const int bs = 1 << log2_bs;
-  const int ctx = ctx_lens[s];
-  const bool bad_len = ctx < 0 || ctx > max_ctx || static_cast<int64_t>(ctx) > static_cast<int64_t>(max_blocks) * bs;
+  const int ctx = P.ctx[s];
+  const bool bad_len =
+      ctx < 0 || ctx > P.max_ctx || static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) * bs;
   const int nparts = bad_len ? 1 : max(1, (ctx + PART - 1) / PART);
   if (p >= nparts) return;
   const int t0 = p * PART;
   const int t1 = bad_len ? t0 : min(t0 + PART, ctx);
   const int b0 = t0 >> log2_bs;
-  const int nb = t1 > t0 ? ((t1 - 1) >> log2_bs) - b0 + 1 : 0;
+  const int64_t trow = static_cast<int64_t>(s) * P.max_blocks;
+  const int g = h / P.group;
+  const int64_t sh = static_cast<int64_t>(s) * P.hq + h;
+  const int64_t head_rows = static_cast<int64_t>(g) * bs;      // token rows before head g in a block
+  const int64_t block_rows = static_cast<int64_t>(P.hkv) * bs;  // token rows per block
 
-  __shared__ int tab[PART];
-  __shared__ int bad_blk;
+  __shared__ int tab[BIG ? 1 : PART];
   __shared__ float red_m[NW], red_l[NW];
   __shared__ float red_o[NW][D];
-  if (tid == 0) bad_blk = 0;
-  __syncthreads();
-  for (int i = tid; i < nb; i += NW * 64) {
-    int b = tables[static_cast<int64_t>(s) * max_blocks + b0 + i];
-    if (b < 0 || b >= num_blocks) {
-      bad_blk = 1;
-      b = 0;
-    }
-    tab[i] = b;
-  }
-  __syncthreads();
-  const int64_t sh = static_cast<int64_t>(s) * hq + h;
-  if (bad_len || bad_blk) {
-    if (tid < D) {
-      if (nparts == 1) {
-        out[sh * D + tid] = from_f32<ACT>(NAN);
-      } else {
-        ws_o[(sh * max_parts + p) * D + tid] = NAN;
-        if (tid == 0) ws_ml[(sh * max_parts + p) * 2] = ws_ml[(sh * max_parts + p) * 2 + 1] = NAN;
+  __shared__ int is_last;
+  int my_bad = bad_len ? 1 : 0;
+  // BIG: the partition's table slice lives in registers, entry i in lane
+  // i % 64 of tabreg[i / 64]; a wave-uniform index is read with readlane.
+  constexpr int NTR = (PART / TPL + 63) / 64;
+  int tabreg[NTR];
+  {
+    const int nb = t1 > t0 ? ((t1 - 1) >> log2_bs) - b0 + 1 : 0;
+    if constexpr (BIG) {
+#pragma unroll
+      for (int j = 0; j < NTR; ++j) {
+        const int i = lane + 64 * j;
+        int b = 0;
+        if (i < nb) {
+          b = P.tables[trow + b0 + i];
+          if (b < 0 || b >= P.num_blocks) {
+            my_bad = 1;
+            b = 0;
+          }
+        }
+        tabreg[j] = b;
+      }
+    } else {
+      for (int i = tid; i < nb; i += NW * 64) {
+        int b = P.tables[trow + b0 + i];
+        if (b < 0 || b >= P.num_blocks) {
+          my_bad = 1;
+          b = 0;
+        }
+        tab[i] = b;
       }
     }
-    return;
   }
 
-  const int g = h / group;
-  const typename M::Q qr = M::load_q(q + sh * D + c * EPL);
+  // Fused append: the partition holding the new token (position ctx - 1)
+  // takes its K/V from the caller's rows, not from the pool, and the kv
+  // head's first query head stores them into the pool slot.  Nothing in this
+  // launch reads that slot from the pool.
+  const bool has_new = P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
+  Vec16 knew{{0, 0, 0, 0}}, vnew{{0, 0, 0, 0}};
+  if (has_new) {
+    const int64_t src = (static_cast<int64_t>(s) * P.hkv + g) * D * static_cast<int64_t>(sizeof(ACT));
+    knew = NewChunk<KV, ACT>::load(P.k_new + src, c, P.k_inv);
+    vnew = NewChunk<KV, ACT>::load(P.v_new + src, c, P.v_inv);
+    if (h % P.group == 0 && w == 0 && row == 0) {
+      const int pos = ctx - 1;
+      const int b = P.tables[trow + (pos >> log2_bs)];
+      if (b >= 0 && b < P.num_blocks) {
+        const int64_t tok_row = static_cast<int64_t>(b) * block_rows + head_rows + (pos & (bs - 1));
+        const size_t off = static_cast<size_t>(tok_row * D + c * EPL) * KVB;
+        store16(P.kw + off, knew);
+        store16(P.vw + off, vnew);
+      }
+    }
+  }
+  const bool bad_early = __syncthreads_or(my_bad) != 0;
+
+  const typename M::Q qr = M::load_q(static_cast<const ACT*>(P.q) + sh * D + c * EPL);
   float m = -INFINITY, l = 0.f;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
-  const int nrounds = (t1 - t0 + ROUND - 1) / ROUND;
+  const int nrounds = bad_early ? 0 : (t1 - t0 + ROUND - 1) / ROUND;
   for (int r0 = 0; r0 < nrounds; r0 += U) {
     Vec16 kr[U], vr[U];
-    bool valid[U];
+    int tok[U];
+    int64_t blk[U];
+    // block ids of the U wave loads first ...
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = t0 + (r0 + u) * ROUND + w * TPL + row;
-      valid[u] = t < t1;
-      const int tt = valid[u] ? t : t0;
-      const int64_t blk = tab[(tt >> log2_bs) - b0];
-      const int64_t tok_row = (blk * hkv + g) * bs + (tt & (bs - 1));
-      const size_t off = static_cast<size_t>(tok_row * D + c * EPL) * KVBytes<KV>::value;
-      if (valid[u]) {
-        kr[u] = load16(kc + off);
-        vr[u] = load16(vc + off);
+      const int tb = t0 + (r0 + u) * ROUND + w * TPL;  // first token of this wave load
+      tok[u] = tb + row;
+      if constexpr (BIG) {
+        const int idx = (min(tb, t1 - 1) >> log2_bs) - b0;
+        blk[u] = __builtin_amdgcn_readlane(tabreg[idx >> 6], idx & 63);
       } else {
-        kr[u] = Vec16{{0, 0, 0, 0}};
-        vr[u] = Vec16{{0, 0, 0, 0}};
+        blk[u] = tab[(min(tok[u], t1 - 1) >> log2_bs) - b0];
+      }
+    }
+    // ... then every K and V load of the batch, before any arithmetic
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(tok[u], t1 - 1);
+      const int64_t tok_row = blk[u] * block_rows + head_rows + (t & (bs - 1));
+      const size_t off = static_cast<size_t>(tok_row * D + c * EPL) * KVB;
+      kr[u] = load16_stream(P.kc + off);
+      vr[u] = load16_stream(P.vc + off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_new && r0 + U >= nrounds) {  // the batch that holds the new token
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (tok[u] == ctx - 1) {
+          kr[u] = knew;
+          vr[u] = vnew;
+        }
       }
     }
     float sc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float d0 = M::dot(kr[u], qr);
-#pragma unroll
-      for (int o = 1; o < LPT; o <<= 1) d0 += __shfl_xor(d0, o);
-      sc[u] = valid[u] ? d0 * score_scale : -INFINITY;
+      const float d0 = group_sum<LPT>(M::dot(kr[u], qr));
+      sc[u] = tok[u] < t1 ? d0 * P.score_scale : -INFINITY;
     }
     float mloc = sc[0];
 #pragma unroll
@@ -254,6 +400,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
     red_l[w] = l;
   }
   __syncthreads();
+  ACT* out = static_cast<ACT*>(P.out);
   for (int i = tid; i < D; i += NW * 64) {
     float mx = -INFINITY;
 #pragma unroll
@@ -266,97 +413,106 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(
       o += f * red_o[v][i];
       L += f * red_l[v];
     }
+    if (bad_early) o = L = mx = NAN;
     if (nparts == 1) {
-      out[sh * D + i] = from_f32<ACT>(ctx > 0 ? o / L * v_scale : 0.f);
+      out[sh * D + i] = from_f32<ACT>(bad_early ? NAN : (ctx > 0 ? o / L * P.v_scale : 0.f));
     } else {
-      ws_o[(sh * max_parts + p) * D + i] = o * v_scale;
+      coherent_store(&P.ws_o[(sh * P.max_parts + p) * D + i], o * P.v_scale);
       if (i == 0) {
-        ws_ml[(sh * max_parts + p) * 2] = mx;
-        ws_ml[(sh * max_parts + p) * 2 + 1] = L;
+        coherent_store(&P.ws_ml[(sh * P.max_parts + p) * 2], mx);
+        coherent_store(&P.ws_ml[(sh * P.max_parts + p) * 2 + 1], L);
       }
     }
   }
-}
+  if (nparts == 1) return;
 
-// One workgroup of D threads per (query head, sequence) with > 1 partition.
-template <typename ACT, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ ws_ml,
-                                                         const float* __restrict__ ws_o, ACT* __restrict__ out,
-                                                         const int32_t* __restrict__ ctx_lens, int hq, int max_ctx,
-                                                         int max_blocks, int log2_bs, int max_parts) {
-  constexpr int PART = kPartitionTokens;
-  const int h = blockIdx.x, s = blockIdx.y, i = threadIdx.x;
-  const int ctx = ctx_lens[s];
-  const bool bad_len = ctx < 0 || ctx > max_ctx ||
-                       static_cast<int64_t>(ctx) > static_cast<int64_t>(max_blocks) << log2_bs;
-  if (bad_len) return;
-  const int nparts = (ctx + PART - 1) / PART;
-  if (nparts <= 1) return;
-  const int64_t sh = static_cast<int64_t>(s) * hq + h;
-  const float* ml = ws_ml + sh * max_parts * 2;
-  float mx = -INFINITY;
-  for (int p = 0; p < nparts; ++p) mx = fmaxf(mx, ml[2 * p]);
-  float o = 0.f, L = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float f = exp2f(ml[2 * p] - mx);
-    L += f * ml[2 * p + 1];
-    o += f * ws_o[(sh * max_parts + p) * D + i];
+  // Split context: the last partition to finish merges all partials of this
+  // (sequence, head) exactly and restores the arrival counter to zero.
+  // Partials are written and read with device-coherent accesses (they bypass
+  // the per-XCD L2, which other XCDs do not see), and every store has
+  // completed (s_waitcnt) before the counter is bumped, so the last arrival
+  // reads every partial without a whole-L2 write-back or invalidate.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(&P.counters[sh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
+  __syncthreads();
+  if (!is_last) return;
+  const float* ml = P.ws_ml + sh * P.max_parts * 2;
+  for (int i = tid; i < D; i += NW * 64) {
+    float mx = -INFINITY;
+    for (int q = 0; q < nparts; ++q) mx = fmaxf(mx, coherent_load(&ml[2 * q]));
+    float o = 0.f, L = 0.f;
+    for (int q = 0; q < nparts; ++q) {
+      const float f = exp2f(coherent_load(&ml[2 * q]) - mx);
+      L += f * coherent_load(&ml[2 * q + 1]);
+      o += f * coherent_load(&P.ws_o[(sh * P.max_parts + q) * D + i]);
+    }
+    out[sh * D + i] = from_f32<ACT>(o / L);
   }
-  out[sh * D + i] = from_f32<ACT>(o / L);
+  if (tid == 0) __hip_atomic_store(&P.counters[sh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename KV, typename ACT, int D>
-hipError_t decode_t(const DecodeArgs& a, bool* merge_launched) {
-  constexpr int NW = 4, U = 8;
+hipError_t decode_t(const DecodeArgs& a) {
+  constexpr int NW = PA_DECODE_WAVES, U = PA_DECODE_UNROLL;
+  constexpr int TPL = 64 / (D / Math<KV, ACT>::EPL);
   const pa_kv_cache& c = *a.cache;
-  const int log2_bs = __builtin_ctz(c.block_size);
-  const int group = a.num_q_heads / c.num_kv_heads;
-  const float score_scale = a.sm_scale * kLog2e * (c.kv_dtype == PA_FP8_E4M3 ? c.k_scale : 1.f);
-  const float v_scale = c.kv_dtype == PA_FP8_E4M3 ? c.v_scale : 1.f;
-  const int parts = (a.max_ctx + kPartitionTokens - 1) / kPartitionTokens;
-  const dim3 grid(parts > 0 ? parts : 1, a.num_q_heads, a.num_seqs);
+  Params P;
+  P.kc = static_cast<const char*>(c.k_cache);
+  P.vc = static_cast<const char*>(c.v_cache);
+  P.kw = static_cast<char*>(c.k_cache);
+  P.vw = static_cast<char*>(c.v_cache);
+  P.q = a.q;
+  P.out = a.out;
+  P.k_new = static_cast<const char*>(a.k_new);
+  P.v_new = static_cast<const char*>(a.v_new);
+  P.tables = a.tables;
+  P.ctx = a.ctx;
+  P.counters = a.counters;
+  P.ws_ml = a.ws_ml;
+  P.ws_o = a.ws_o;
+  P.num_blocks = c.num_blocks;
+  P.log2_bs = __builtin_ctz(c.block_size);
+  P.hkv = c.num_kv_heads;
+  P.hq = a.num_q_heads;
+  P.group = a.num_q_heads / c.num_kv_heads;
+  P.max_blocks = a.max_blocks;
+  P.max_ctx = a.max_ctx;
+  P.max_parts = a.max_parts;
+  P.score_scale = a.sm_scale * kLog2e * (c.kv_dtype == PA_FP8_E4M3 ? c.k_scale : 1.f);
+  P.v_scale = c.kv_dtype == PA_FP8_E4M3 ? c.v_scale : 1.f;
+  P.k_inv = c.k_inv_scale;
+  P.v_inv = c.v_inv_scale;
+  const unsigned np = static_cast<unsigned>(a.max_parts);
+  const dim3 grid(PA_GRID_HEAD_FIRST ? a.num_q_heads : np, PA_GRID_HEAD_FIRST ? np : a.num_q_heads, a.num_seqs);
+  auto kern = c.block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true> : decode_kernel<KV, ACT, D, NW, U, false>;
   if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
-  hipLaunchKernelGGL((decode_partition_kernel<KV, ACT, D, NW, U>), grid, dim3(NW * 64), 0, a.stream,
-                     static_cast<const char*>(c.k_cache), static_cast<const char*>(c.v_cache),
-                     static_cast<const ACT*>(a.q), static_cast<ACT*>(a.out), a.tables, a.ctx, a.ws_ml, a.ws_o,
-                     c.num_blocks, log2_bs, c.num_kv_heads, a.num_q_heads, group, a.max_blocks, a.max_ctx,
-                     a.max_parts, score_scale, v_scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, a.stream, P);
+  const hipError_t e = hipGetLastError();
   if (a.ev[1]) (void)hipEventRecord(a.ev[1], a.stream);
-  *merge_launched = false;
-  if (parts > 1) {
-    if (a.ev[2]) (void)hipEventRecord(a.ev[2], a.stream);
-    hipLaunchKernelGGL((decode_merge_kernel<ACT, D>), dim3(a.num_q_heads, a.num_seqs), dim3(D), 0, a.stream,
-                       a.ws_ml, a.ws_o, static_cast<ACT*>(a.out), a.ctx, a.num_q_heads, a.max_ctx, a.max_blocks,
-                       log2_bs, a.max_parts);
-    e = hipGetLastError();
-    if (a.ev[3]) (void)hipEventRecord(a.ev[3], a.stream);
-    *merge_launched = true;
-  }
   return e;
 }
 
 template <typename KV, typename ACT>
-hipError_t decode_d(const DecodeArgs& a, bool* ml) {
+hipError_t decode_d(const DecodeArgs& a) {
   switch (a.cache->head_dim) {
-    case 32: return decode_t<KV, ACT, 32>(a, ml);
-    case 64: return decode_t<KV, ACT, 64>(a, ml);
-    case 128: return decode_t<KV, ACT, 128>(a, ml);
+    case 32: return decode_t<KV, ACT, 32>(a);
+    case 64: return decode_t<KV, ACT, 64>(a);
+    case 128: return decode_t<KV, ACT, 128>(a);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, bool* merge_launched) {
-  *merge_launched = false;
+hipError_t launch_decode(const DecodeArgs& a) {
   if (a.num_seqs == 0 || a.num_q_heads == 0) return hipSuccess;
   const int kv = a.cache->kv_dtype;
-  if (kv == PA_F32 && a.act == PA_F32) return decode_d<float, float>(a, merge_launched);
-  if (kv == PA_F16 && a.act == PA_F16) return decode_d<half_t, half_t>(a, merge_launched);
-  if (kv == PA_FP8_E4M3 && a.act == PA_F16) return decode_d<fp8_t, half_t>(a, merge_launched);
-  if (kv == PA_FP8_E4M3 && a.act == PA_F32) return decode_d<fp8_t, float>(a, merge_launched);
+  if (kv == PA_F32 && a.act == PA_F32) return decode_d<float, float>(a);
+  if (kv == PA_F16 && a.act == PA_F16) return decode_d<half_t, half_t>(a);
+  if (kv == PA_FP8_E4M3 && a.act == PA_F16) return decode_d<fp8_t, half_t>(a);
+  if (kv == PA_FP8_E4M3 && a.act == PA_F32) return decode_d<fp8_t, float>(a);
   return hipErrorInvalidValue;
 }
 

@@ -40,6 +40,20 @@ __device__ __forceinline__ Vec16 load16(const void* p) {
   return Vec16{{v.x, v.y, v.z, v.w}};
 }
 
+// K/V rows are read once per step: mark the loads non-temporal (streamed).
+#ifndef PA_KV_NONTEMPORAL
+#define PA_KV_NONTEMPORAL 1
+#endif
+__device__ __forceinline__ Vec16 load16_stream(const void* p) {
+#if PA_KV_NONTEMPORAL
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return Vec16{{v[0], v[1], v[2], v[3]}};
+#else
+  return load16(p);
+#endif
+}
+
 __device__ __forceinline__ void store16(void* p, const Vec16& v) {
   *reinterpret_cast<uint4*>(p) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
 }
@@ -75,6 +89,20 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
   r = (c != c) ? ((r & 0xFF00FFFFu) | 0x007F0000u) : r;
   r = (d != d) ? ((r & 0x00FFFFFFu) | 0x7F000000u) : r;
   return r;
+}
+
+// Eight f16 numbers (one 16-byte chunk) -> eight E4M3 bytes of x * inv.
+__device__ __forceinline__ uint2 f16x8_to_e4m3(const Vec16& v, float inv) {
+  return make_uint2(f32x4_to_e4m3(half_lo(v.w[0]) * inv, half_hi(v.w[0]) * inv, half_lo(v.w[1]) * inv,
+                                  half_hi(v.w[1]) * inv),
+                    f32x4_to_e4m3(half_lo(v.w[2]) * inv, half_hi(v.w[2]) * inv, half_lo(v.w[3]) * inv,
+                                  half_hi(v.w[3]) * inv));
+}
+
+// Four f32 numbers (one 16-byte chunk) -> four E4M3 bytes of x * inv.
+__device__ __forceinline__ uint32_t f32x4_chunk_to_e4m3(const Vec16& v, float inv) {
+  return f32x4_to_e4m3(__builtin_bit_cast(float, v.w[0]) * inv, __builtin_bit_cast(float, v.w[1]) * inv,
+                       __builtin_bit_cast(float, v.w[2]) * inv, __builtin_bit_cast(float, v.w[3]) * inv);
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

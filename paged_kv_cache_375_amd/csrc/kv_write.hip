@@ -26,20 +26,14 @@ struct ChunkStore<T, T> {  // same dtype: a 16-byte copy
 template <>
 struct ChunkStore<half_t, fp8_t> {  // 8 f16 -> 8 bytes
   static __device__ __forceinline__ void run(void* dst, const void* src, float inv) {
-    const Vec16 v = load16(src);
-    uint32_t lo = f32x4_to_e4m3(half_lo(v.w[0]) * inv, half_hi(v.w[0]) * inv, half_lo(v.w[1]) * inv,
-                                half_hi(v.w[1]) * inv);
-    uint32_t hi = f32x4_to_e4m3(half_lo(v.w[2]) * inv, half_hi(v.w[2]) * inv, half_lo(v.w[3]) * inv,
-                                half_hi(v.w[3]) * inv);
-    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(dst) = f16x8_to_e4m3(load16(src), inv);
   }
 };
 
 template <>
 struct ChunkStore<float, fp8_t> {  // 4 f32 -> 4 bytes
   static __device__ __forceinline__ void run(void* dst, const void* src, float inv) {
-    const float4 v = *reinterpret_cast<const float4*>(src);
-    *reinterpret_cast<uint32_t*>(dst) = f32x4_to_e4m3(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+    *reinterpret_cast<uint32_t*>(dst) = f32x4_chunk_to_e4m3(load16(src), inv);
   }
 };
 

@@ -9,7 +9,10 @@
 namespace pa {
 
 // Tokens per split-context partition of the decode kernels.
-constexpr int kPartitionTokens = 256;
+#ifndef PA_PARTITION_TOKENS
+#define PA_PARTITION_TOKENS 512
+#endif
+constexpr int kPartitionTokens = PA_PARTITION_TOKENS;
 
 hipError_t launch_append(const pa_kv_cache& c, const void* k_new, const void* v_new, int act, const int32_t* tables,
                          const int32_t* ctx, int num_seqs, int max_blocks, hipStream_t st);
@@ -22,6 +25,8 @@ struct DecodeArgs {
   const pa_kv_cache* cache;
   const void* q;
   void* out;
+  const void* k_new;  // non-null: append the step's new K/V in the same launch
+  const void* v_new;
   int act;
   int num_q_heads;
   const int32_t* tables;
@@ -29,15 +34,16 @@ struct DecodeArgs {
   int num_seqs;
   int max_blocks;
   int max_ctx;
-  int max_parts;  // partitions the workspace holds per (sequence, head)
+  int max_parts;   // partitions the workspace holds per (sequence, head)
   float sm_scale;
-  float* ws_ml;   // [num_seqs][num_q_heads][max_parts][2]: running max (log2 units), sum
-  float* ws_o;    // [num_seqs][num_q_heads][max_parts][head_dim]: unnormalised output
+  int* counters;   // [num_seqs][num_q_heads] arrival counters, zero between calls
+  float* ws_ml;    // [num_seqs][num_q_heads][max_parts][2]: running max (log2 units), sum
+  float* ws_o;     // [num_seqs][num_q_heads][max_parts][head_dim]: unnormalised output
   hipStream_t stream;
-  hipEvent_t ev[4];  // optional timing events: partition start/stop, merge start/stop (or null)
+  hipEvent_t ev[2];  // optional timing events around the kernel (or null)
 };
 
 // Returns hipErrorInvalidValue for an unsupported dtype/shape combination.
-hipError_t launch_decode(const DecodeArgs& a, bool* merge_launched);
+hipError_t launch_decode(const DecodeArgs& a);
 
 }  // namespace pa

@@ -6,7 +6,8 @@ the library's prompt-write kernel (prefix first, then the copy-on-write
 copies made while sequences grew, then each sequence's own tokens).
 
 ``DecodeStep.run()`` is one step of the hot path: the step's copy-on-write
-copies (if any), the append of every sequence's new K/V, and the decode.
+copies (if any), the append of every sequence's new K/V, and the decode —
+by default the append and the decode share one launch (pa_decode_step).
 """
 import math
 
@@ -52,13 +53,18 @@ class DecodeStep:
         self.max_ctx = int(sc.ctx.max())
         self.sm_scale = float(np.float32(1.0 / math.sqrt(wl.head_dim)))
         self.out = torch.empty_like(self.q)
-        need = api.decode_workspace_size(wl.batch, wl.num_q_heads, wl.head_dim, self.max_ctx)
-        self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        self.workspace = api.new_workspace(wl.batch, wl.num_q_heads, wl.head_dim, self.max_ctx, device)
 
-    def run(self, cache=None, stream=None):
+    def run(self, cache=None, stream=None, fused=True):
+        """One step: copy-on-write copies, then append + decode (one launch when fused)."""
         c = cache or self.cache
         if self.step_pairs is not None:
             api.copy_blocks(c, self.step_pairs, stream)
-        api.kv_append(c, self.k_new, self.v_new, self.tables, self.ctx, stream)
-        api.decode(c, self.q, self.tables, self.ctx, self.max_ctx, self.sm_scale, self.out, self.workspace, stream)
+        if fused:
+            api.decode_step(c, self.q, self.k_new, self.v_new, self.tables, self.ctx, self.max_ctx, self.sm_scale,
+                            self.out, self.workspace, stream)
+        else:
+            api.kv_append(c, self.k_new, self.v_new, self.tables, self.ctx, stream)
+            api.decode(c, self.q, self.tables, self.ctx, self.max_ctx, self.sm_scale, self.out, self.workspace,
+                       stream)
         return self.out

@@ -62,10 +62,10 @@ def test_decode_argument_checks_fail_before_any_launch():
     assert _decode(_cache(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.0)) == _lib.PA_ERR_INVALID_ARGUMENT
     # long contexts need the split-context workspace
     need = L.pa_decode_workspace_size(2, 4, 128, 2048)
-    assert need == 2 * 4 * 8 * (128 + 2) * 4
+    assert need == 256 + 2 * 4 * 4 * (128 + 2) * 4  # counters, then 512-token partitions
     assert _decode(_cache(), mctx=2048, wsb=need - 1, ws=0x7000) == _lib.PA_ERR_WORKSPACE_TOO_SMALL
     assert b"workspace" in L.pa_last_error()
-    assert L.pa_decode_workspace_size(2, 4, 128, 256) == 0  # one partition: no workspace
+    assert L.pa_decode_workspace_size(2, 4, 128, 512) == 0  # one partition: no workspace
     # zero sequences: nothing to do, nothing launched
     assert _decode(_cache(), B=0) == _lib.PA_OK
 

@@ -15,15 +15,16 @@ from tests.gpu_helpers import SMALL, TOL, build_pair, out_f64, pool_bytes
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["decode_step", "append+decode"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_step_parity_small(name):
+def test_step_parity_small(name, fused):
     wl = SMALL[name]
-    print(f"[parity] {name} {wl}", flush=True)
+    print(f"[parity] {name} fused={fused} {wl}", flush=True)
     dr, gpu, ref = build_pair(wl)
     # history written by the prompt-write kernel (and copies) is bit-exact
     assert np.array_equal(pool_bytes(gpu.cache.k), ref.history_k.view(np.uint8))
     assert np.array_equal(pool_bytes(gpu.cache.v), ref.history_v.view(np.uint8))
-    out = out_f64(gpu.run())
+    out = out_f64(gpu.run(fused=fused))
     ref.append()
     # the step's copies and append are bit-exact and nothing else changed
     assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
@@ -35,9 +36,11 @@ def test_step_parity_small(name):
     assert err <= TOL[wl.kv]
     if name == "toy":
         assert err <= 1e-5  # fp32 pool and activations: a much tighter gate holds
-    # a second step with the same inputs is idempotent
-    out2 = out_f64(gpu.run())
+    # a second step with the same inputs is idempotent (and the workspace's
+    # arrival counters were left at zero by the first)
+    out2 = out_f64(gpu.run(fused=fused))
     assert np.array_equal(out, out2)
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
 
 
 def test_fp8_store_exhaustive_over_f16_inputs():
@@ -135,3 +138,26 @@ def test_special_cases():
     torch.cuda.synchronize()
     longest = int(torch.argmax(gpu.ctx).item())
     assert torch.isnan(outc[longest]).all()
+
+
+def test_workspace_reuse_across_context_lengths():
+    """One zero-filled workspace serves calls with the same sequences and heads
+    but other context lengths in turn: the counters each call leaves at zero
+    let the next call merge correctly."""
+    big = SMALL["opt13b"].scaled(batch=6, ctx_lo=900, ctx_hi=2000)
+    small = SMALL["opt13b"].scaled(batch=6, ctx_lo=520, ctx_hi=1100)
+    dr_b, gpu_b, ref_b = build_pair(big)
+    dr_s, gpu_s, ref_s = build_pair(small)
+    ws = gpu_b.workspace
+    assert ws.numel() >= gpu_s.workspace.numel()
+    for _ in range(2):
+        out_b = out_f64(api.decode_step(gpu_b.cache, gpu_b.q, gpu_b.k_new, gpu_b.v_new, gpu_b.tables, gpu_b.ctx,
+                                        gpu_b.max_ctx, gpu_b.sm_scale, workspace=ws))
+        out_s = out_f64(api.decode_step(gpu_s.cache, gpu_s.q, gpu_s.k_new, gpu_s.v_new, gpu_s.tables, gpu_s.ctx,
+                                        gpu_s.max_ctx, gpu_s.sm_scale, workspace=ws))
+    ref_b.append()
+    ref_s.append()
+    assert np.max(np.abs(out_b - ref_b.decode())) <= TOL["f16"]
+    assert np.max(np.abs(out_s - ref_s.decode())) <= TOL["f16"]
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[:6 * 40 * 4]) == 0  # counters back at zero
