@@ -27,13 +27,10 @@
 
 #include <cmath>
 
-#include "device.h"
-#include "launch.h"
+#include "decode_common.h"
 
 namespace pa {
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
 
 // Launch shape: wavefronts per workgroup and wave loads per batch.
 #ifndef PA_DECODE_WAVES
@@ -158,15 +155,6 @@ struct Math<fp8_t, ACT> {  // E4M3 pool: exact hardware conversion to f32
   }
 };
 
-// Device-coherent (agent scope) accesses for data exchanged between
-// workgroups of one launch, which may run on different XCDs.
-__device__ __forceinline__ void coherent_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Merge (m, l, acc) with another state: exact rescaling to the larger max.
 template <int EPL>
 __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, float mo, float lo, const float* acco) {
@@ -179,52 +167,9 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
   m = mn;
 }
 
-// The new token's 16-byte chunk c in pool format (quantised for FP8 pools),
-// read from a [head_dim] row of activations.
-template <typename KV, typename ACT>
-struct NewChunk;
-template <typename T>
-struct NewChunk<T, T> {
-  static __device__ __forceinline__ Vec16 load(const char* row, int c, float) { return load16(row + c * 16); }
-};
-template <>
-struct NewChunk<fp8_t, half_t> {  // 16 numbers = 32 bytes of f16
-  static __device__ __forceinline__ Vec16 load(const char* row, int c, float inv) {
-    const uint2 a = f16x8_to_e4m3(load16(row + c * 32), inv), b = f16x8_to_e4m3(load16(row + c * 32 + 16), inv);
-    return Vec16{{a.x, a.y, b.x, b.y}};
-  }
-};
-template <>
-struct NewChunk<fp8_t, float> {  // 16 numbers = 64 bytes of f32
-  static __device__ __forceinline__ Vec16 load(const char* row, int c, float inv) {
-    Vec16 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.w[i] = f32x4_chunk_to_e4m3(load16(row + c * 64 + 16 * i), inv);
-    return r;
-  }
-};
-
-struct Params {
-  const char* kc;  // K pool
-  const char* vc;  // V pool
-  char* kw;        // the same pools, written by the fused append
-  char* vw;
-  const void* q;
-  void* out;
-  const char* k_new;  // [num_seqs][hkv][D] activations, or null (no append)
-  const char* v_new;
-  const int32_t* tables;
-  const int32_t* ctx;
-  int* counters;  // [num_seqs][hq] partition arrival counts (zero between calls)
-  float* ws_ml;   // [num_seqs][hq][max_parts][2]
-  float* ws_o;    // [num_seqs][hq][max_parts][D]
-  int num_blocks, log2_bs, hkv, hq, group, max_blocks, max_ctx, max_parts;
-  float score_scale, v_scale, k_inv, v_inv;
-};
-
 // BIG: block_size >= TPL (block id wave-uniform, table slice in registers).
 template <typename KV, typename ACT, int D, int NW, int U, bool BIG>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(const Params P) {
+__global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   using M = Math<KV, ACT>;
   constexpr int EPL = M::EPL;
   constexpr int LPT = D / EPL;
@@ -352,7 +297,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const Params P) {
     if (has_new && r0 + U >= nrounds) {  // the batch that holds the new token
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (tok[u] == ctx - 1) {
+        // lanes past the context re-read the last token: they take the new
+        // token too (their weight is zero, but a stale slot could hold NaN)
+        if (min(tok[u], t1 - 1) == ctx - 1) {
           kr[u] = knew;
           vr[u] = vnew;
         }
@@ -458,32 +405,7 @@ hipError_t decode_t(const DecodeArgs& a) {
   constexpr int NW = PA_DECODE_WAVES, U = PA_DECODE_UNROLL;
   constexpr int TPL = 64 / (D / Math<KV, ACT>::EPL);
   const pa_kv_cache& c = *a.cache;
-  Params P;
-  P.kc = static_cast<const char*>(c.k_cache);
-  P.vc = static_cast<const char*>(c.v_cache);
-  P.kw = static_cast<char*>(c.k_cache);
-  P.vw = static_cast<char*>(c.v_cache);
-  P.q = a.q;
-  P.out = a.out;
-  P.k_new = static_cast<const char*>(a.k_new);
-  P.v_new = static_cast<const char*>(a.v_new);
-  P.tables = a.tables;
-  P.ctx = a.ctx;
-  P.counters = a.counters;
-  P.ws_ml = a.ws_ml;
-  P.ws_o = a.ws_o;
-  P.num_blocks = c.num_blocks;
-  P.log2_bs = __builtin_ctz(c.block_size);
-  P.hkv = c.num_kv_heads;
-  P.hq = a.num_q_heads;
-  P.group = a.num_q_heads / c.num_kv_heads;
-  P.max_blocks = a.max_blocks;
-  P.max_ctx = a.max_ctx;
-  P.max_parts = a.max_parts;
-  P.score_scale = a.sm_scale * kLog2e * (c.kv_dtype == PA_FP8_E4M3 ? c.k_scale : 1.f);
-  P.v_scale = c.kv_dtype == PA_FP8_E4M3 ? c.v_scale : 1.f;
-  P.k_inv = c.k_inv_scale;
-  P.v_inv = c.v_inv_scale;
+  const DecodeParams P = make_decode_params(a);
   const unsigned np = static_cast<unsigned>(a.max_parts);
   const dim3 grid(PA_GRID_HEAD_FIRST ? a.num_q_heads : np, PA_GRID_HEAD_FIRST ? np : a.num_q_heads, a.num_seqs);
   auto kern = c.block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true> : decode_kernel<KV, ACT, D, NW, U, false>;
@@ -508,6 +430,7 @@ hipError_t decode_d(const DecodeArgs& a) {
 
 hipError_t launch_decode(const DecodeArgs& a) {
   if (a.num_seqs == 0 || a.num_q_heads == 0) return hipSuccess;
+  if (group_decode_applies(a)) return launch_decode_group(a);
   const int kv = a.cache->kv_dtype;
   if (kv == PA_F32 && a.act == PA_F32) return decode_d<float, float>(a);
   if (kv == PA_F16 && a.act == PA_F16) return decode_d<half_t, half_t>(a);

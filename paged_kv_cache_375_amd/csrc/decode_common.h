@@ -1,0 +1,119 @@
+// Pieces shared by the two decode kernels (per-head VALU kernel and grouped
+// MFMA kernel): launch parameters, the new token's pool-format chunks for the
+// fused append, and device-coherent accesses to the split-context partials.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "device.h"
+#include "launch.h"
+
+namespace pa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecodeParams {
+  const char* kc;  // K pool
+  const char* vc;  // V pool
+  char* kw;        // the same pools, written by the fused append
+  char* vw;
+  const void* q;
+  void* out;
+  const char* k_new;  // [num_seqs][hkv][D] activations, or null (no append)
+  const char* v_new;
+  const int32_t* tables;
+  const int32_t* ctx;
+  int* counters;  // [num_seqs][hq] partition arrival counts (zero between calls)
+  float* ws_ml;   // [num_seqs][hq][max_parts][2]
+  float* ws_o;    // [num_seqs][hq][max_parts][D]
+  int num_blocks, log2_bs, hkv, hq, group, max_blocks, max_ctx, max_parts;
+  // scores are kept in log2 units: score_scale = sm_scale * log2(e) (* k_scale
+  // for FP8 pools); v_scale multiplies the output (FP8 pools, else 1)
+  float score_scale, v_scale, k_inv, v_inv;
+};
+
+inline DecodeParams make_decode_params(const DecodeArgs& a) {
+  const pa_kv_cache& c = *a.cache;
+  DecodeParams P;
+  P.kc = static_cast<const char*>(c.k_cache);
+  P.vc = static_cast<const char*>(c.v_cache);
+  P.kw = static_cast<char*>(c.k_cache);
+  P.vw = static_cast<char*>(c.v_cache);
+  P.q = a.q;
+  P.out = a.out;
+  P.k_new = static_cast<const char*>(a.k_new);
+  P.v_new = static_cast<const char*>(a.v_new);
+  P.tables = a.tables;
+  P.ctx = a.ctx;
+  P.counters = a.counters;
+  P.ws_ml = a.ws_ml;
+  P.ws_o = a.ws_o;
+  P.num_blocks = c.num_blocks;
+  P.log2_bs = __builtin_ctz(c.block_size);
+  P.hkv = c.num_kv_heads;
+  P.hq = a.num_q_heads;
+  P.group = a.num_q_heads / c.num_kv_heads;
+  P.max_blocks = a.max_blocks;
+  P.max_ctx = a.max_ctx;
+  P.max_parts = a.max_parts;
+  P.score_scale = a.sm_scale * kLog2e * (c.kv_dtype == PA_FP8_E4M3 ? c.k_scale : 1.f);
+  P.v_scale = c.kv_dtype == PA_FP8_E4M3 ? c.v_scale : 1.f;
+  P.k_inv = c.k_inv_scale;
+  P.v_inv = c.v_inv_scale;
+  return P;
+}
+
+// Device-coherent (agent scope) accesses for data exchanged between
+// workgroups of one launch, which may run on different XCDs.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The new token's 16-byte chunk c in pool format (quantised for FP8 pools),
+// read from a [head_dim] row of activations.
+template <typename KV, typename ACT>
+struct NewChunk;
+template <typename T>
+struct NewChunk<T, T> {
+  static __device__ __forceinline__ Vec16 load(const char* row, int c, float) { return load16(row + c * 16); }
+};
+template <>
+struct NewChunk<fp8_t, half_t> {  // 16 numbers = 32 bytes of f16
+  static __device__ __forceinline__ Vec16 load(const char* row, int c, float inv) {
+    const uint2 a = f16x8_to_e4m3(load16(row + c * 32), inv), b = f16x8_to_e4m3(load16(row + c * 32 + 16), inv);
+    return Vec16{{a.x, a.y, b.x, b.y}};
+  }
+};
+template <>
+struct NewChunk<fp8_t, float> {  // 16 numbers = 64 bytes of f32
+  static __device__ __forceinline__ Vec16 load(const char* row, int c, float inv) {
+    Vec16 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.w[i] = f32x4_chunk_to_e4m3(load16(row + c * 64 + 16 * i), inv);
+    return r;
+  }
+};
+
+// Store the new token's K and V (pool format) into its slot: the first
+// D * sizeof(KV) / 16 threads each move one 16-byte chunk.  Sequences whose
+// table entry is out of range store nothing.
+template <typename KV, typename ACT, int D>
+__device__ __forceinline__ void store_new_token(const DecodeParams& P, int s, int g, int ctx, int tid) {
+  constexpr int CHUNKS = D * Elem<KV>::bytes / 16;
+  if (tid >= CHUNKS) return;
+  const int pos = ctx - 1;
+  const int bs = 1 << P.log2_bs;
+  const int b = P.tables[static_cast<int64_t>(s) * P.max_blocks + (pos >> P.log2_bs)];
+  if (b < 0 || b >= P.num_blocks) return;
+  const int64_t src = (static_cast<int64_t>(s) * P.hkv + g) * D * static_cast<int64_t>(sizeof(ACT));
+  const int64_t tok_row = (static_cast<int64_t>(b) * P.hkv + g) * bs + (pos & (bs - 1));
+  const size_t off = static_cast<size_t>(tok_row * D) * Elem<KV>::bytes + tid * 16;
+  store16(P.kw + off, NewChunk<KV, ACT>::load(P.k_new + src, tid, P.k_inv));
+  store16(P.vw + off, NewChunk<KV, ACT>::load(P.v_new + src, tid, P.v_inv));
+}
+
+}  // namespace pa

@@ -1,0 +1,494 @@
+// Paged decode attention for grouped- and multi-query attention, where the
+// query heads of a group share one KV head [F55 §后来的做法]: the group's
+// scores and weighted sums are small dense products, done on the matrix
+// cores (v_mfma_f32_16x16x32_f16, f32 accumulation).
+//
+// One workgroup per (KV head and group of up to 16 * HT query heads,
+// partition of kPartitionTokens tokens, sequence).  Its NW wavefronts take
+// 32-token chunks of the partition in turn; a chunk is processed as
+//
+//   S^T[32 tokens][16 heads] = K[32][D] . Q^T[D][16]      (2 x D/32 MFMAs per head tile)
+//   online softmax of each head's column (scores in log2 units, exp2)
+//   O^T[D][16 heads] += V^T[D][32] . P^T[32][16]          (D/16 MFMAs per head tile)
+//
+// Computing S transposed puts the weights P^T straight into the B-operand
+// layout of the second product: the lane that holds head n's scores for
+// tokens {4g..4g+3, 16+4g..16+4g+3} (g = lane / 16) is the lane that feeds
+// those tokens into the contraction, so P never moves between lanes.  The
+// head_dim order of the first product's contraction is free (Q and K use the
+// same order), so every K row is read with 16-byte loads straight into the
+// A operand.  V^T needs each lane to hold eight tokens of one head_dim
+// column, so the V rows of a chunk are loaded with coalesced 16-byte loads,
+// written to the wave's slice of LDS (16-byte chunks XOR-swizzled by row so
+// the column reads do not collide on banks), and read back column-wise.
+//
+// Heads past the group (padding up to 16 per tile) have q = 0 and are never
+// written.  The NW wavefronts' partial results are merged in a fixed order
+// through LDS, and partitions by the last workgroup to finish, exactly as in
+// the per-head kernel (same workspace layout), so results are deterministic.
+// Blocks are fetched through the table in logical order and need not be
+// adjacent [F55 §块表]; [IPX §分离逻辑顺序与实际存储位置].
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "decode_common.h"
+
+namespace pa {
+namespace {
+
+#ifndef PA_GROUP_WAVES
+#define PA_GROUP_WAVES 4
+#endif
+#ifndef PA_GROUP_UNROLL
+#define PA_GROUP_UNROLL 2
+#endif
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 32;  // tokens per chunk: two 16-row tiles of the first product
+
+__device__ __forceinline__ float4_t mfma16x16x32(const half8_t& a, const half8_t& b, const float4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8_t as_half8(const Vec16& v) { return __builtin_bit_cast(half8_t, v); }
+
+// Eight E4M3 numbers (two 32-bit words) -> eight f16 (exact: every E4M3
+// value is an f16 value).
+__device__ __forceinline__ half8_t e4m3x8_to_half8(uint32_t lo, uint32_t hi) {
+  half8_t r;
+  const uint32_t w[2] = {lo, hi};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float2_t a = e4m3x2_to_f32(w[i], false), b = e4m3x2_to_f32(w[i], true);
+    r[4 * i] = static_cast<_Float16>(a[0]);
+    r[4 * i + 1] = static_cast<_Float16>(a[1]);
+    r[4 * i + 2] = static_cast<_Float16>(b[0]);
+    r[4 * i + 3] = static_cast<_Float16>(b[1]);
+  }
+  return r;
+}
+
+template <typename KV, int D>
+struct Layout {
+  static constexpr int KVB = Elem<KV>::bytes;
+  static constexpr int NS = D / 32;                  // k-steps of the first product
+  static constexpr int NDT = D / 16;                 // 16-wide head_dim tiles of the second
+  static constexpr bool PAIR = KVB == 1 && NS >= 2;  // FP8: one 16-byte load feeds two k-steps
+  static constexpr int KLOADS = PAIR ? NS / 2 : NS;  // K loads per lane per 16-token tile
+  static constexpr int VCH = D * KVB / 16;           // 16-byte pool chunks per token row
+  static constexpr int NV = kChunk * VCH / 64;       // V loads per lane per chunk
+  static constexpr int LCH = D / 8;                  // 16-byte f16 chunks per LDS row
+  static_assert(NV >= 1 && (kChunk * VCH) % 64 == 0, "head_dim does not fit the V load layout");
+  // first element of the 8 head_dim values lane group g feeds into k-step st
+  static __device__ __forceinline__ int dbase(int st, int g) {
+    return PAIR ? 64 * (st >> 1) + 16 * g + 8 * (st & 1) : 32 * st + 8 * g;
+  }
+  // byte offset within a pool row of the lane group's K load kl
+  static __device__ __forceinline__ int kbyte(int kl, int g) { return PAIR ? 64 * kl + 16 * g : dbase(kl, g) * KVB; }
+  // XOR swizzle of the 16-byte chunks of LDS row r
+  static __device__ __forceinline__ int swz(int r) { return (((r >> 2) & 3) << 1) & (LCH - 1); }
+};
+
+template <typename KV, int D, int HT, int NW, int U>
+__global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParams P, int groups_per_kv) {
+  using L = Layout<KV, D>;
+  constexpr int KVB = L::KVB, NS = L::NS, NDT = L::NDT, KLOADS = L::KLOADS, NV = L::NV, LCH = L::LCH;
+  constexpr int VCH = L::VCH;
+  constexpr int PART = kPartitionTokens;
+  constexpr int MREGS = HT * NDT * 4 + 2 * HT;  // floats per lane in a wave's partial result
+
+  const int grp = blockIdx.x % groups_per_kv;
+  const int kvh = blockIdx.x / groups_per_kv;
+  const int p = blockIdx.y;
+  const int s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int log2_bs = P.log2_bs;
+  const int bs = 1 << log2_bs;
+  const int ctx = P.ctx[s];
+  const bool bad_len =
+      ctx < 0 || ctx > P.max_ctx || static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) * bs;
+  const int nparts = bad_len ? 1 : max(1, (ctx + PART - 1) / PART);
+  if (p >= nparts) return;
+  const int t0 = p * PART;
+  const int t1 = bad_len ? t0 : min(t0 + PART, ctx);
+  const int b0 = t0 >> log2_bs;
+  const int64_t trow = static_cast<int64_t>(s) * P.max_blocks;
+  const int h0 = kvh * P.group + grp * HT * 16;              // first query head of the workgroup
+  const int nh = min(HT * 16, P.group - grp * HT * 16);      // query heads of the workgroup
+  const int64_t head_rows = static_cast<int64_t>(kvh) * bs;  // token rows before head kvh in a block
+  const int64_t block_rows = static_cast<int64_t>(P.hkv) * bs;
+
+  __shared__ int tab[PART];
+  __shared__ uint4 vbuf[NW][kChunk * LCH];  // each wave's V chunk as f16 rows
+  __shared__ float mbuf[MREGS][64];         // one wave's partial result, for the merge
+  __shared__ int is_last;
+
+  int my_bad = bad_len ? 1 : 0;
+  {
+    const int nb = t1 > t0 ? ((t1 - 1) >> log2_bs) - b0 + 1 : 0;
+    for (int i = tid; i < nb; i += NW * 64) {
+      int b = P.tables[trow + b0 + i];
+      if (b < 0 || b >= P.num_blocks) {
+        my_bad = 1;
+        b = 0;
+      }
+      tab[i] = b;
+    }
+  }
+  // Fused append: the workgroup of the KV head's first query group stores the
+  // new token into its slot; every workgroup reading the new token takes it
+  // from the caller's rows instead of the pool.
+  const bool has_new = P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
+  if (has_new && grp == 0 && w == 0) store_new_token<KV, half_t, D>(P, s, kvh, ctx, lane);
+  const bool bad = __syncthreads_or(my_bad) != 0;
+
+  // B operand of the first product: q of head 16 * ht + n at the head_dim
+  // positions lane group g feeds into each k-step (zero past the group)
+  half8_t qf[HT][NS];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int hh = 16 * ht + n;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      if (hh < nh) {
+        const half_t* qrow = static_cast<const half_t*>(P.q) + (static_cast<int64_t>(s) * P.hq + h0 + hh) * D;
+        qf[ht][st] = as_half8(load16(qrow + L::dbase(st, g)));
+      } else {
+        qf[ht][st] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  }
+
+  float4_t o[HT][NDT];
+  float m[HT], lsum[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    m[ht] = -INFINITY;
+    lsum[ht] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const char* knew_row = nullptr;
+  const char* vnew_row = nullptr;
+  if (has_new) {
+    const int64_t src = (static_cast<int64_t>(s) * P.hkv + kvh) * D * static_cast<int64_t>(sizeof(half_t));
+    knew_row = P.k_new + src;
+    vnew_row = P.v_new + src;
+  }
+  uint4* const vb = vbuf[w];
+  const int nchunks = bad ? 0 : (t1 - t0 + kChunk - 1) / kChunk;
+
+  for (int c0 = w * U; c0 < nchunks; c0 += NW * U) {
+    Vec16 kr[U][2][KLOADS];
+    Vec16 vr[U][NV];
+    // every K and V load of the batch first
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u >= nchunks) break;
+      const int cb = t0 + (c0 + u) * kChunk;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const int t = min(cb + 16 * tau + n, t1 - 1);
+        const int64_t row = tab[(t >> log2_bs) - b0] * block_rows + head_rows + (t & (bs - 1));
+        const char* rp = P.kc + row * (D * KVB);
+        const bool sub = has_new && t == ctx - 1;
+#pragma unroll
+        for (int kl = 0; kl < KLOADS; ++kl) {
+          if constexpr (KVB == 2) {
+            kr[u][tau][kl] = load16_stream((sub ? knew_row : rp) + L::kbyte(kl, g));
+          } else if constexpr (L::PAIR) {
+            kr[u][tau][kl] = sub ? NewChunk<KV, half_t>::load(knew_row, 4 * kl + g, P.k_inv)
+                                 : load16_stream(rp + L::kbyte(kl, g));
+          } else {  // FP8, head_dim 32: 8-byte loads
+            if (sub) {
+              const Vec16 c = NewChunk<KV, half_t>::load(knew_row, g >> 1, P.k_inv);
+              kr[u][tau][kl] = Vec16{{c.w[2 * (g & 1)], c.w[2 * (g & 1) + 1], 0, 0}};
+            } else {
+              const uint2 x = *reinterpret_cast<const uint2*>(rp + L::kbyte(kl, g));
+              kr[u][tau][kl] = Vec16{{x.x, x.y, 0, 0}};
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int f = v * 64 + lane;
+        const int r = f / VCH, ch = f % VCH;
+        const int t = min(cb + r, t1 - 1);
+        const int64_t row = tab[(t >> log2_bs) - b0] * block_rows + head_rows + (t & (bs - 1));
+        if (has_new && t == ctx - 1) {
+          vr[u][v] = NewChunk<KV, half_t>::load(vnew_row, ch, P.v_inv);
+        } else {
+          vr[u][v] = load16_stream(P.vc + row * (D * KVB) + ch * 16);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u >= nchunks) break;
+      const int cb = t0 + (c0 + u) * kChunk;
+      // V rows of the chunk into the wave's LDS slice as f16 (the previous
+      // chunk's column reads were issued before these writes, and one wave's
+      // LDS accesses complete in order)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int f = v * 64 + lane;
+        const int r = f / VCH, ch = f % VCH;
+        if constexpr (KVB == 2) {
+          vb[r * LCH + (ch ^ L::swz(r))] = make_uint4(vr[u][v].w[0], vr[u][v].w[1], vr[u][v].w[2], vr[u][v].w[3]);
+        } else {
+          const half8_t a = e4m3x8_to_half8(vr[u][v].w[0], vr[u][v].w[1]);
+          const half8_t b = e4m3x8_to_half8(vr[u][v].w[2], vr[u][v].w[3]);
+          vb[r * LCH + ((2 * ch) ^ L::swz(r))] = __builtin_bit_cast(uint4, a);
+          vb[r * LCH + ((2 * ch + 1) ^ L::swz(r))] = __builtin_bit_cast(uint4, b);
+        }
+      }
+
+      // scores S^T: lane (g, n) gets tokens 16 tau + 4 g + i of head 16 ht + n
+      float sc[HT][8];
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        half8_t ka[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          if constexpr (KVB == 2) {
+            ka[st] = as_half8(kr[u][tau][st]);
+          } else if constexpr (L::PAIR) {
+            const Vec16& x = kr[u][tau][st >> 1];
+            ka[st] = (st & 1) ? e4m3x8_to_half8(x.w[2], x.w[3]) : e4m3x8_to_half8(x.w[0], x.w[1]);
+          } else {
+            ka[st] = e4m3x8_to_half8(kr[u][tau][st].w[0], kr[u][tau][st].w[1]);
+          }
+        }
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < NS; ++st) acc = mfma16x16x32(ka[st], qf[ht][st], acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = cb + 16 * tau + 4 * g + i;
+            sc[ht][4 * tau + i] = tok < t1 ? acc[i] * P.score_scale : -INFINITY;
+          }
+        }
+      }
+
+      // online softmax per head column; the weights become the B operand
+      half8_t pf[HT];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        float mloc = sc[ht][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[ht][j]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+        const float m_new = fmaxf(m[ht], mloc);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f(m[ht] - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const _Float16 ph = static_cast<_Float16>(exp2f(sc[ht][j] - m_use));
+          pf[ht][j] = ph;
+          psum += static_cast<float>(ph);  // the weights the product uses
+        }
+        lsum[ht] = lsum[ht] * alpha + psum;
+        m[ht] = m_new;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= alpha;
+      }
+
+      // V^T columns from LDS: lane (g, n) takes column 16 dt + n of the
+      // tokens it holds weights for, 16 (j / 4) + 4 g + j % 4
+      const _Float16* vh = reinterpret_cast<const _Float16*>(vb);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        half8_t va;
+        const int chunk = 2 * dt + (n >> 3);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = 16 * (j >> 2) + 4 * g + (j & 3);
+          va[j] = vh[r * D + ((chunk ^ L::swz(r)) << 3) + (n & 7)];
+        }
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) o[ht][dt] = mfma16x16x32(va, pf[ht], o[ht][dt]);
+      }
+    }
+  }
+
+  // each head's weight sum over the wave's four lane groups
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    lsum[ht] += __shfl_xor(lsum[ht], 16);
+    lsum[ht] += __shfl_xor(lsum[ht], 32);
+  }
+
+  // merge the wavefronts' partial results in a fixed order: wave NW-1 into
+  // NW-2, ..., 1 into 0 (lane l merges with lane l; layouts are identical)
+  for (int src = NW - 1; src >= 1; --src) {
+    if (w == src) {
+      int k = 0;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        mbuf[k++][lane] = m[ht];
+        mbuf[k++][lane] = lsum[ht];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mbuf[k++][lane] = o[ht][dt][i];
+      }
+    }
+    __syncthreads();
+    if (w == src - 1) {
+      int k = 0;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        const float mo = mbuf[k++][lane];
+        const float lo = mbuf[k++][lane];
+        const float mn = fmaxf(m[ht], mo);
+        const float mu = (mn == -INFINITY) ? 0.f : mn;
+        const float a = exp2f(m[ht] - mu), b = exp2f(mo - mu);
+        lsum[ht] = lsum[ht] * a + lo * b;
+        m[ht] = mn;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[ht][dt][i] = o[ht][dt][i] * a + mbuf[k++][lane] * b;
+      }
+    }
+    __syncthreads();
+  }
+
+  half_t* out = static_cast<half_t*>(P.out);
+  if (w == 0) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int hh = 16 * ht + n;
+      if (hh >= nh) continue;
+      const int64_t sh = static_cast<int64_t>(s) * P.hq + h0 + hh;
+      const float mx = bad ? NAN : m[ht];
+      const float lx = bad ? NAN : lsum[ht];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int d = 16 * dt + 4 * g;
+        if (nparts == 1) {
+          const float f = bad ? NAN : (ctx > 0 ? P.v_scale / lx : 0.f);
+          typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+          half4_t r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r[i] = static_cast<_Float16>(bad ? NAN : o[ht][dt][i] * f);
+          *reinterpret_cast<half4_t*>(out + sh * D + d) = r;
+        } else {
+          float* dst = P.ws_o + (sh * P.max_parts + p) * D + d;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) coherent_store(dst + i, bad ? NAN : o[ht][dt][i] * P.v_scale);
+        }
+      }
+      if (nparts > 1 && g == 0) {
+        coherent_store(&P.ws_ml[(sh * P.max_parts + p) * 2], mx);
+        coherent_store(&P.ws_ml[(sh * P.max_parts + p) * 2 + 1], lx);
+      }
+    }
+  }
+  if (nparts == 1) return;
+
+  // Split context: the last partition to finish merges every partial of the
+  // workgroup's heads exactly and restores the arrival counter to zero (see
+  // the per-head kernel for the memory-ordering argument).
+  const int64_t cidx = static_cast<int64_t>(s) * P.hq + h0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(&P.counters[cidx], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
+  __syncthreads();
+  if (!is_last) return;
+  for (int i = tid; i < nh * D; i += NW * 64) {
+    const int hh = i / D, d = i % D;
+    const int64_t sh = static_cast<int64_t>(s) * P.hq + h0 + hh;
+    const float* ml = P.ws_ml + sh * P.max_parts * 2;
+    float mx = -INFINITY;
+    for (int q = 0; q < nparts; ++q) mx = fmaxf(mx, coherent_load(&ml[2 * q]));
+    float ov = 0.f, lv = 0.f;
+    for (int q = 0; q < nparts; ++q) {
+      const float f = exp2f(coherent_load(&ml[2 * q]) - mx);
+      lv += f * coherent_load(&ml[2 * q + 1]);
+      ov += f * coherent_load(&P.ws_o[(sh * P.max_parts + q) * D + d]);
+    }
+    out[sh * D + d] = static_cast<half_t>(ov / lv);
+  }
+  if (tid == 0) __hip_atomic_store(&P.counters[cidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Head tiles per workgroup: as many as the group needs, up to a register
+// budget that depends on head_dim.
+template <int D>
+constexpr int max_head_tiles() {
+  return D >= 128 ? 2 : 5;
+}
+
+template <typename KV, int D, int HT>
+hipError_t launch_ht(const DecodeArgs& a, int groups) {
+  constexpr int NW = PA_GROUP_WAVES, U = PA_GROUP_UNROLL;
+  const DecodeParams P = make_decode_params(a);
+  const dim3 grid(static_cast<unsigned>(a.cache->num_kv_heads * groups), static_cast<unsigned>(a.max_parts),
+                  static_cast<unsigned>(a.num_seqs));
+  if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
+  hipLaunchKernelGGL((decode_group_kernel<KV, D, HT, NW, U>), grid, dim3(NW * 64), 0, a.stream, P, groups);
+  const hipError_t e = hipGetLastError();
+  if (a.ev[1]) (void)hipEventRecord(a.ev[1], a.stream);
+  return e;
+}
+
+template <typename KV, int D>
+hipError_t launch_d(const DecodeArgs& a) {
+  constexpr int HTMAX = max_head_tiles<D>();
+  const int G = a.num_q_heads / a.cache->num_kv_heads;
+  const int tiles = (G + 15) / 16;
+  const int groups = (tiles + HTMAX - 1) / HTMAX;
+  const int ht = (tiles + groups - 1) / groups;
+  switch (ht) {
+    case 1: return launch_ht<KV, D, 1>(a, groups);
+    case 2: return launch_ht<KV, D, 2>(a, groups);
+  }
+  if constexpr (HTMAX >= 5) {
+    switch (ht) {
+      case 3: return launch_ht<KV, D, 3>(a, groups);
+      case 4: return launch_ht<KV, D, 4>(a, groups);
+      case 5: return launch_ht<KV, D, 5>(a, groups);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename KV>
+hipError_t launch_kv(const DecodeArgs& a) {
+  switch (a.cache->head_dim) {
+    case 32: return launch_d<KV, 32>(a);
+    case 64: return launch_d<KV, 64>(a);
+    case 128: return launch_d<KV, 128>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool group_decode_applies(const DecodeArgs& a) {
+  const int kv = a.cache->kv_dtype;
+  return a.act == PA_F16 && (kv == PA_F16 || kv == PA_FP8_E4M3) && a.num_q_heads > a.cache->num_kv_heads;
+}
+
+hipError_t launch_decode_group(const DecodeArgs& a) {
+  if (a.cache->kv_dtype == PA_F16) return launch_kv<half_t>(a);
+  if (a.cache->kv_dtype == PA_FP8_E4M3) return launch_kv<fp8_t>(a);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -46,4 +46,9 @@ struct DecodeArgs {
 // Returns hipErrorInvalidValue for an unsupported dtype/shape combination.
 hipError_t launch_decode(const DecodeArgs& a);
 
+// The grouped-query kernel (matrix cores) serves f16 activations over f16 or
+// FP8 pools when several query heads share each KV head.
+bool group_decode_applies(const DecodeArgs& a);
+hipError_t launch_decode_group(const DecodeArgs& a);
+
 }  // namespace pa

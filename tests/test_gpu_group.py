@@ -1,0 +1,124 @@
+"""Parity of the grouped-query (matrix-core) decode kernel and of the full
+workloads against the CPU reference (needs an MI355X).
+
+Small cases cover every head-tile count the kernel is built for, query
+groups split over several workgroups, partial head tiles, every head_dim,
+FP8 pools and block sizes from 1 to 64; each spans several 512-token
+partitions with a ragged last chunk.  The full workloads run at their real
+sizes, in the launch the benchmark times, and are checked on sampled
+(sequence, head) outputs that the reference computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_375_amd.workloads import WORKLOADS, Workload
+from tests.gpu_helpers import TOL, build_pair, out_f64, pool_bytes
+
+pytestmark = pytest.mark.gpu
+
+# (q heads, kv heads, head_dim, pool dtype, block size)
+GROUP_CASES = [
+    (16, 8, 128, "f16", 16),   # G 2
+    (64, 8, 128, "f16", 16),   # G 8, the Llama-2-70B layer's grouping
+    (32, 2, 128, "f16", 16),   # G 16: one full head tile
+    (68, 2, 128, "f16", 16),   # G 34: three tiles over two workgroups per KV head
+    (71, 1, 64, "f16", 16),    # G 71: five tiles, the Falcon-7B layer's grouping
+    (40, 1, 64, "f16", 32),    # G 40: three tiles
+    (24, 1, 32, "f16", 4),     # G 24, head_dim 32, small blocks
+    (64, 4, 64, "f16", 1),     # G 16, one token per block
+    (64, 8, 128, "f16", 64),   # G 8, 64-token blocks
+    (64, 8, 128, "e4m3", 16),  # FP8 pool, head_dim 128
+    (40, 4, 64, "e4m3", 8),    # FP8 pool, head_dim 64
+    (12, 3, 32, "e4m3", 16),   # FP8 pool, head_dim 32 (8-byte K loads)
+]
+
+
+def _wl(hq, hkv, d, kv, bs):
+    return Workload(f"group_{hq}x{hkv}x{d}_{kv}_bs{bs}", hq, hkv, d, bs, 4, 1, 1300, kv=kv)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["decode_step", "append+decode"])
+@pytest.mark.parametrize("case", GROUP_CASES, ids=lambda c: "q{}_kv{}_d{}_{}_bs{}".format(*c))
+def test_group_kernel_parity(case, fused):
+    wl = _wl(*case)
+    print(f"[group] {wl} fused={fused}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    out = out_f64(gpu.run(fused=fused))
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    want = ref.decode()
+    err = float(np.max(np.abs(out - want)))
+    print(f"[group] {wl.name}: max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]
+    out2 = out_f64(gpu.run(fused=fused))
+    assert np.array_equal(out, out2)  # deterministic, counters left at zero
+
+
+def test_group_kernel_placement_invariance_bit_exact():
+    wl = _wl(64, 8, 128, "f16", 16)
+    dr, gpu, ref = build_pair(wl)
+    out = gpu.run().clone()
+    from paged_kv_cache_375_amd import api
+    perm = torch.randperm(dr.num_blocks, generator=torch.Generator().manual_seed(3)).cuda()
+    k2, v2 = torch.empty_like(gpu.cache.k), torch.empty_like(gpu.cache.v)
+    k2[perm] = gpu.cache.k
+    v2[perm] = gpu.cache.v
+    t = gpu.tables.long()
+    tables2 = torch.where(t >= 0, perm[t.clamp(min=0)], t).to(torch.int32).contiguous()
+    out2 = api.decode(gpu.cache.with_pools(k2, v2), gpu.q, tables2, gpu.ctx, gpu.max_ctx, gpu.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def test_group_kernel_special_cases():
+    from paged_kv_cache_375_amd import api
+    wl = Workload("group_ctx1", 64, 8, 128, 16, 4, 1, 1)
+    dr, gpu, ref = build_pair(wl)
+    out = gpu.run()
+    torch.cuda.synchronize()
+    # one token: its weight is exactly one, the output is the appended V
+    assert torch.equal(out, gpu.v_new.repeat_interleave(8, dim=1))
+    wl = Workload("group_bad", 64, 8, 128, 16, 3, 300, 1100)
+    dr, gpu, ref = build_pair(wl)
+    gpu.run()
+    bad = gpu.tables.clone()
+    bad[1, 0] = dr.num_blocks + 3
+    outb = api.decode(gpu.cache, gpu.q, bad, gpu.ctx, gpu.max_ctx, gpu.sm_scale)
+    ctx0 = torch.zeros_like(gpu.ctx)
+    out0 = api.decode(gpu.cache, gpu.q, gpu.tables, ctx0, gpu.max_ctx, gpu.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.isnan(outb[1]).all()
+    assert not torch.isnan(outb[0]).any() and not torch.isnan(outb[2]).any()
+    assert torch.count_nonzero(out0) == 0
+
+
+FULL = ["opt13b", "llama70b_gqa", "falcon7b_mqa", "opt13b_fp8_prefix"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_workload_sampled_parity(name):
+    """The real sizes in the benchmark's launch (append + decode fused): the
+    whole pool after the step is bit-exact, and sampled outputs — the longest
+    and shortest sequences' every head, plus random (sequence, head) pairs —
+    meet the bound against the reference."""
+    wl = WORKLOADS[name]
+    print(f"[full] {name}: building", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    out = out_f64(gpu.run())
+    ref.append()
+    print(f"[full] {name}: comparing pools", flush=True)
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    rng = np.random.default_rng(11)
+    B, hq = wl.batch, wl.num_q_heads
+    longest, shortest = int(np.argmax(dr.ctx)), int(np.argmin(dr.ctx))
+    seqs = [longest] * hq + [shortest] * hq + rng.integers(0, B, 64).tolist()
+    heads = list(range(hq)) * 2 + rng.integers(0, hq, 64).tolist()
+    want = ref.decode_pairs(seqs, heads)
+    got = out[np.array(seqs), np.array(heads)]
+    err = float(np.max(np.abs(got - want)))
+    print(f"[full] {name}: {len(seqs)} sampled outputs, max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]
