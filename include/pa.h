@@ -165,7 +165,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  * by the last partition of that (sequence, head) to finish (the online
  * softmax gives the same result [F55 related plate F51]).
  *
- * max_context_len must be >= every context_lens[s]; workspace must hold
+ * max_context_len must be >= every context_lens[s] and at most 524,288
+ * (1024 partitions; larger values return PA_ERR_UNSUPPORTED); workspace must hold
  * pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len)
  * bytes (NULL allowed when that size is 0).  The workspace must be
  * zero-filled before its first use: its arrival counters (the first

@@ -142,6 +142,8 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
   if (num_seqs > kMaxGridYZ || num_q_heads > kMaxGridYZ)
     return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs %d / num_q_heads %d above %d", fn, num_seqs, num_q_heads,
                 kMaxGridYZ);
+  if (max_context_len > pa::kMaxContextLen)
+    return fail(PA_ERR_UNSUPPORTED, "%s: max_context_len %d above %d", fn, max_context_len, pa::kMaxContextLen);
   if (!(sm_scale == sm_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: sm_scale is NaN", fn);
   if (num_seqs == 0) return ok();
   if (!q || !out || !block_tables || !context_lens || (k_new == nullptr) != (v_new == nullptr))

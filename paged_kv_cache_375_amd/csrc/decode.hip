@@ -385,18 +385,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
     is_last = __hip_atomic_fetch_add(&P.counters[sh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
   __syncthreads();
   if (!is_last) return;
-  const float* ml = P.ws_ml + sh * P.max_parts * 2;
-  for (int i = tid; i < D; i += NW * 64) {
-    float mx = -INFINITY;
-    for (int q = 0; q < nparts; ++q) mx = fmaxf(mx, coherent_load(&ml[2 * q]));
-    float o = 0.f, L = 0.f;
-    for (int q = 0; q < nparts; ++q) {
-      const float f = exp2f(coherent_load(&ml[2 * q]) - mx);
-      L += f * coherent_load(&ml[2 * q + 1]);
-      o += f * coherent_load(&P.ws_o[(sh * P.max_parts + q) * D + i]);
-    }
-    out[sh * D + i] = from_f32<ACT>(o / L);
-  }
+  __shared__ float merge_m[kMergeCap], merge_w[kMergeCap];
+  merge_partials<ACT, D, NW * 64>(P, sh, 1, nparts, tid, merge_m, merge_w);
   if (tid == 0) __hip_atomic_store(&P.counters[sh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

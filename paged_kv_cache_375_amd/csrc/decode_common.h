@@ -117,3 +117,82 @@ __device__ __forceinline__ void store_new_token(const DecodeParams& P, int s, in
 }
 
 }  // namespace pa
+
+namespace pa {
+
+// Floats of LDS scratch merge_partials needs (two arrays of this size); at
+// least the largest partition count.
+constexpr int kMergeCap = kMaxPartitions;
+
+// The exact merge of split-context partials, run by the last workgroup of a
+// (sequence, head group) to finish: heads sh0 .. sh0 + nh - 1 (rows of the
+// [num_seqs * hq] workspace), nparts partitions each.  Every partition p
+// left (m_p, l_p) (running max in log2 units and weight sum) and the
+// unnormalised vector o_p; the result is
+//   out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p,
+// the same rescaling the online softmax does within a partition.  All loads
+// of a stage are independent (partials are read with device-coherent loads:
+// other workgroups wrote them, possibly on another XCD).  mw, ww: LDS
+// scratch of kMergeCap floats each.  NT threads take part; the caller
+// synchronises before the call.
+template <typename ACT, int D, int NT>
+__device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh0, int nh, int nparts, int tid,
+                                               float* mw, float* ww) {
+  ACT* out = static_cast<ACT*>(P.out);
+  const int hb = max(1, min(nh, kMergeCap / nparts));  // heads per batch
+  for (int hbase = 0; hbase < nh; hbase += hb) {
+    const int nb = min(hb, nh - hbase);
+    for (int i = tid; i < nb * nparts; i += NT) {
+      const int hh = i / nparts, q = i - hh * nparts;
+      const float* ml = P.ws_ml + ((sh0 + hbase + hh) * P.max_parts + q) * 2;
+      mw[i] = coherent_load(ml);
+      ww[i] = coherent_load(ml + 1);
+    }
+    __syncthreads();
+    for (int hh = tid; hh < nb; hh += NT) {
+      float M = -INFINITY;
+      for (int q = 0; q < nparts; ++q) M = fmaxf(M, mw[hh * nparts + q]);
+      float L = 0.f;
+      for (int q = 0; q < nparts; ++q) {
+        const float f = exp2f(mw[hh * nparts + q] - M);
+        mw[hh * nparts + q] = f;
+        L += f * ww[hh * nparts + q];
+      }
+      const float inv = 1.f / L;
+      for (int q = 0; q < nparts; ++q) ww[hh * nparts + q] = mw[hh * nparts + q] * inv;
+    }
+    __syncthreads();
+    // four consecutive output elements per thread; partials in groups of four
+    for (int i = tid; i < nb * (D / 4); i += NT) {
+      const int hh = i / (D / 4), d = (i - hh * (D / 4)) * 4;
+      const int64_t sh = sh0 + hbase + hh;
+      const float* o = P.ws_o + sh * P.max_parts * D + d;
+      const float* w = ww + hh * nparts;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      int q = 0;
+      for (; q + 4 <= nparts; q += 4) {
+        float x[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[u][e] = coherent_load(o + (q + u) * D + e);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += w[q + u] * x[u][e];
+      }
+      for (; q < nparts; ++q) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = coherent_load(o + q * D + e);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += w[q] * x[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[sh * D + d + e] = from_f32<ACT>(acc[e]);
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace pa

@@ -20,7 +20,11 @@
 // A operand.  V^T needs each lane to hold eight tokens of one head_dim
 // column, so the V rows of a chunk are loaded with coalesced 16-byte loads,
 // written to the wave's slice of LDS (16-byte chunks XOR-swizzled by row so
-// the column reads do not collide on banks), and read back column-wise.
+// the reads do not collide on banks), and read back with gfx950's transposing
+// LDS read (ds_read_b64_tr_b16: lane i of each 16-lane group receives element
+// i of the four 8-byte rows addressed by lanes 4k..4k+3, k = 0..3), two reads
+// per 16-column tile.  The loop is software-pipelined: the next chunk's K and
+// V loads are in flight while the current chunk is computed.
 //
 // Heads past the group (padding up to 16 per tile) have q = 0 and are never
 // written.  The NW wavefronts' partial results are merged in a fixed order
@@ -40,9 +44,6 @@ namespace {
 #ifndef PA_GROUP_WAVES
 #define PA_GROUP_WAVES 4
 #endif
-#ifndef PA_GROUP_UNROLL
-#define PA_GROUP_UNROLL 2
-#endif
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -54,6 +55,19 @@ __device__ __forceinline__ float4_t mfma16x16x32(const half8_t& a, const half8_t
 }
 
 __device__ __forceinline__ half8_t as_half8(const Vec16& v) { return __builtin_bit_cast(half8_t, v); }
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+// Transposing LDS read of 8 bytes per lane (see the header comment).
+__device__ __forceinline__ short4_t lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(const_cast<void*>(p)));
+}
+
+// exp2 on the hardware unit (inputs here are <= 0 or -inf; results below the
+// smallest normal float may flush to zero, which no weight here relies on)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Eight E4M3 numbers (two 32-bit words) -> eight f16 (exact: every E4M3
 // value is an f16 value).
@@ -88,11 +102,12 @@ struct Layout {
   }
   // byte offset within a pool row of the lane group's K load kl
   static __device__ __forceinline__ int kbyte(int kl, int g) { return PAIR ? 64 * kl + 16 * g : dbase(kl, g) * KVB; }
-  // XOR swizzle of the 16-byte chunks of LDS row r
-  static __device__ __forceinline__ int swz(int r) { return (((r >> 2) & 3) << 1) & (LCH - 1); }
+  // XOR swizzle of the 16-byte chunks of LDS row r: eight consecutive rows
+  // put any 32-byte column pair in distinct banks (fewer for short rows)
+  static __device__ __forceinline__ int swz(int r) { return (2 * r) & (LCH - 2); }
 };
 
-template <typename KV, int D, int HT, int NW, int U>
+template <typename KV, int D, int HT, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParams P, int groups_per_kv) {
   using L = Layout<KV, D>;
   constexpr int KVB = L::KVB, NS = L::NS, NDT = L::NDT, KLOADS = L::KLOADS, NV = L::NV, LCH = L::LCH;
@@ -125,8 +140,10 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
 
   __shared__ int tab[PART];
   __shared__ uint4 vbuf[NW][kChunk * LCH];  // each wave's V chunk as f16 rows
+  static_assert(sizeof(vbuf) >= 2 * kMergeCap * sizeof(float), "merge scratch does not fit");
   __shared__ float mbuf[MREGS][64];         // one wave's partial result, for the merge
   __shared__ int is_last;
+  __shared__ Vec16 newkv[2][VCH];  // the new token's K and V rows in pool format
 
   int my_bad = bad_len ? 1 : 0;
   {
@@ -145,6 +162,11 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
   // from the caller's rows instead of the pool.
   const bool has_new = P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
   if (has_new && grp == 0 && w == 0) store_new_token<KV, half_t, D>(P, s, kvh, ctx, lane);
+  if (has_new && tid < 2 * VCH) {
+    const int64_t src = (static_cast<int64_t>(s) * P.hkv + kvh) * D * static_cast<int64_t>(sizeof(half_t));
+    const int which = tid / VCH, ch = tid % VCH;
+    newkv[which][ch] = NewChunk<KV, half_t>::load((which ? P.v_new : P.k_new) + src, ch, which ? P.v_inv : P.k_inv);
+  }
   const bool bad = __syncthreads_or(my_bad) != 0;
 
   // B operand of the first product: q of head 16 * ht + n at the head_dim
@@ -174,154 +196,182 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
     for (int dt = 0; dt < NDT; ++dt) o[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const char* knew_row = nullptr;
-  const char* vnew_row = nullptr;
-  if (has_new) {
-    const int64_t src = (static_cast<int64_t>(s) * P.hkv + kvh) * D * static_cast<int64_t>(sizeof(half_t));
-    knew_row = P.k_new + src;
-    vnew_row = P.v_new + src;
-  }
   uint4* const vb = vbuf[w];
   const int nchunks = bad ? 0 : (t1 - t0 + kChunk - 1) / kChunk;
+  // the chunk holding the new token (only it needs substitution); -1 if none
+  const int new_chunk = has_new ? (ctx - 1 - t0) / kChunk : -1;
 
-  for (int c0 = w * U; c0 < nchunks; c0 += NW * U) {
-    Vec16 kr[U][2][KLOADS];
-    Vec16 vr[U][NV];
-    // every K and V load of the batch first
+  // Pool row (in token rows of the pool) of the lane's token t of chunk c's
+  // 16-token tile tau.  With blocks of 16 or more tokens a tile lies in one
+  // block, so one table entry serves the tile (a wave-uniform read).
+  auto tile_row = [&](int cb, int tau, int t) -> int64_t {
+    const int tt = bs >= 16 ? min(cb + 16 * tau, t1 - 1) : t;
+    return tab[(tt >> log2_bs) - b0] * block_rows + head_rows + (t & (bs - 1));
+  };
+  // Issue the K loads (the lane's two token rows) and the V loads of chunk
+  // c; the new token's slot is read like any other (its pool value is
+  // replaced when the chunk is consumed).
+  auto load_k = [&](Vec16 (&kr)[2][KLOADS], int c) {
+    const int cb = t0 + c * kChunk;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c0 + u >= nchunks) break;
-      const int cb = t0 + (c0 + u) * kChunk;
+    for (int tau = 0; tau < 2; ++tau) {
+      const int t = min(cb + 16 * tau + n, t1 - 1);
+      const char* rp = P.kc + tile_row(cb, tau, t) * (D * KVB);
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const int t = min(cb + 16 * tau + n, t1 - 1);
-        const int64_t row = tab[(t >> log2_bs) - b0] * block_rows + head_rows + (t & (bs - 1));
-        const char* rp = P.kc + row * (D * KVB);
-        const bool sub = has_new && t == ctx - 1;
-#pragma unroll
-        for (int kl = 0; kl < KLOADS; ++kl) {
-          if constexpr (KVB == 2) {
-            kr[u][tau][kl] = load16_stream((sub ? knew_row : rp) + L::kbyte(kl, g));
-          } else if constexpr (L::PAIR) {
-            kr[u][tau][kl] = sub ? NewChunk<KV, half_t>::load(knew_row, 4 * kl + g, P.k_inv)
-                                 : load16_stream(rp + L::kbyte(kl, g));
-          } else {  // FP8, head_dim 32: 8-byte loads
-            if (sub) {
-              const Vec16 c = NewChunk<KV, half_t>::load(knew_row, g >> 1, P.k_inv);
-              kr[u][tau][kl] = Vec16{{c.w[2 * (g & 1)], c.w[2 * (g & 1) + 1], 0, 0}};
-            } else {
-              const uint2 x = *reinterpret_cast<const uint2*>(rp + L::kbyte(kl, g));
-              kr[u][tau][kl] = Vec16{{x.x, x.y, 0, 0}};
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int f = v * 64 + lane;
-        const int r = f / VCH, ch = f % VCH;
-        const int t = min(cb + r, t1 - 1);
-        const int64_t row = tab[(t >> log2_bs) - b0] * block_rows + head_rows + (t & (bs - 1));
-        if (has_new && t == ctx - 1) {
-          vr[u][v] = NewChunk<KV, half_t>::load(vnew_row, ch, P.v_inv);
-        } else {
-          vr[u][v] = load16_stream(P.vc + row * (D * KVB) + ch * 16);
+      for (int kl = 0; kl < KLOADS; ++kl) {
+        if constexpr (KVB == 2 || L::PAIR) {
+          kr[tau][kl] = load16_stream(rp + L::kbyte(kl, g));
+        } else {  // FP8, head_dim 32: 8-byte loads
+          const uint2 x = *reinterpret_cast<const uint2*>(rp + L::kbyte(kl, g));
+          kr[tau][kl] = Vec16{{x.x, x.y, 0, 0}};
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto load_v = [&](Vec16 (&vr)[NV], int c) {
+    const int cb = t0 + c * kChunk;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int f = v * 64 + lane;
+      const int r = f / VCH, ch = f % VCH;
+      const int t = min(cb + r, t1 - 1);
+      vr[v] = load16_stream(P.vc + tile_row(cb, r >> 4, t) * (D * KVB) + ch * 16);
+    }
+  };
+  // The chunk holding the new token: lanes at its position (and lanes past
+  // the context, which re-read it) take the caller's K/V in pool format,
+  // staged in LDS at the start.
+  auto substitute = [&](Vec16 (&kr)[2][KLOADS], Vec16 (&vr)[NV], int c) {
+    const int cb = t0 + c * kChunk;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      if (min(cb + 16 * tau + n, t1 - 1) != ctx - 1) continue;
+#pragma unroll
+      for (int kl = 0; kl < KLOADS; ++kl) {
+        if constexpr (KVB == 2 || L::PAIR) {
+          kr[tau][kl] = newkv[0][L::kbyte(kl, g) / 16];
+        } else {  // 8-byte K pieces
+          const Vec16 cn = newkv[0][g >> 1];
+          kr[tau][kl] = Vec16{{cn.w[2 * (g & 1)], cn.w[2 * (g & 1) + 1], 0, 0}};
+        }
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int f = v * 64 + lane;
+      const int r = f / VCH, ch = f % VCH;
+      if (min(cb + r, t1 - 1) == ctx - 1) vr[v] = newkv[1][ch];
+    }
+  };
 
+  // Compute chunk c from its loaded K and V; the registers are refilled with
+  // chunk nx's loads as soon as they are consumed (V once it is in LDS, K once
+  // the score products have read it), so those loads fly during the rest.
+  auto process_chunk = [&](Vec16 (&kr)[2][KLOADS], Vec16 (&vr)[NV], int c, int nx) {
+    const int cb = t0 + c * kChunk;
+    if (c == new_chunk) substitute(kr, vr, c);  // wave-uniform, at most once
+    // V rows into the wave's LDS slice as f16 (the previous chunk's reads
+    // were issued before these writes; one wave's LDS accesses complete in
+    // order)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c0 + u >= nchunks) break;
-      const int cb = t0 + (c0 + u) * kChunk;
-      // V rows of the chunk into the wave's LDS slice as f16 (the previous
-      // chunk's column reads were issued before these writes, and one wave's
-      // LDS accesses complete in order)
+    for (int v = 0; v < NV; ++v) {
+      const int f = v * 64 + lane;
+      const int r = f / VCH, ch = f % VCH;
+      if constexpr (KVB == 2) {
+        vb[r * LCH + (ch ^ L::swz(r))] = make_uint4(vr[v].w[0], vr[v].w[1], vr[v].w[2], vr[v].w[3]);
+      } else {
+        const half8_t a = e4m3x8_to_half8(vr[v].w[0], vr[v].w[1]);
+        const half8_t b = e4m3x8_to_half8(vr[v].w[2], vr[v].w[3]);
+        vb[r * LCH + ((2 * ch) ^ L::swz(r))] = __builtin_bit_cast(uint4, a);
+        vb[r * LCH + ((2 * ch + 1) ^ L::swz(r))] = __builtin_bit_cast(uint4, b);
+      }
+    }
+    if (nx < nchunks) load_v(vr, nx);
+
+    // scores S^T: lane (g, n) gets tokens 16 tau + 4 g + i of head 16 ht + n
+    float sc[HT][8];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int f = v * 64 + lane;
-        const int r = f / VCH, ch = f % VCH;
+    for (int tau = 0; tau < 2; ++tau) {
+      half8_t ka[NS];
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
         if constexpr (KVB == 2) {
-          vb[r * LCH + (ch ^ L::swz(r))] = make_uint4(vr[u][v].w[0], vr[u][v].w[1], vr[u][v].w[2], vr[u][v].w[3]);
+          ka[st] = as_half8(kr[tau][st]);
+        } else if constexpr (L::PAIR) {
+          const Vec16& x = kr[tau][st >> 1];
+          ka[st] = (st & 1) ? e4m3x8_to_half8(x.w[2], x.w[3]) : e4m3x8_to_half8(x.w[0], x.w[1]);
         } else {
-          const half8_t a = e4m3x8_to_half8(vr[u][v].w[0], vr[u][v].w[1]);
-          const half8_t b = e4m3x8_to_half8(vr[u][v].w[2], vr[u][v].w[3]);
-          vb[r * LCH + ((2 * ch) ^ L::swz(r))] = __builtin_bit_cast(uint4, a);
-          vb[r * LCH + ((2 * ch + 1) ^ L::swz(r))] = __builtin_bit_cast(uint4, b);
+          ka[st] = e4m3x8_to_half8(kr[tau][st].w[0], kr[tau][st].w[1]);
         }
       }
-
-      // scores S^T: lane (g, n) gets tokens 16 tau + 4 g + i of head 16 ht + n
-      float sc[HT][8];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        half8_t ka[NS];
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          if constexpr (KVB == 2) {
-            ka[st] = as_half8(kr[u][tau][st]);
-          } else if constexpr (L::PAIR) {
-            const Vec16& x = kr[u][tau][st >> 1];
-            ka[st] = (st & 1) ? e4m3x8_to_half8(x.w[2], x.w[3]) : e4m3x8_to_half8(x.w[0], x.w[1]);
-          } else {
-            ka[st] = e4m3x8_to_half8(kr[u][tau][st].w[0], kr[u][tau][st].w[1]);
-          }
-        }
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int st = 0; st < NS; ++st) acc = mfma16x16x32(ka[st], qf[ht][st], acc);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = cb + 16 * tau + 4 * g + i;
-            sc[ht][4 * tau + i] = tok < t1 ? acc[i] * P.score_scale : -INFINITY;
-          }
-        }
-      }
-
-      // online softmax per head column; the weights become the B operand
-      half8_t pf[HT];
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        float mloc = sc[ht][0];
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[ht][j]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float m_new = fmaxf(m[ht], mloc);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m[ht] - m_use);
-        float psum = 0.f;
+        for (int st = 0; st < NS; ++st) acc = mfma16x16x32(ka[st], qf[ht][st], acc);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const _Float16 ph = static_cast<_Float16>(exp2f(sc[ht][j] - m_use));
-          pf[ht][j] = ph;
-          psum += static_cast<float>(ph);  // the weights the product uses
+        for (int i = 0; i < 4; ++i) {
+          const int tok = cb + 16 * tau + 4 * g + i;
+          sc[ht][4 * tau + i] = tok < t1 ? acc[i] * P.score_scale : -INFINITY;
         }
-        lsum[ht] = lsum[ht] * alpha + psum;
-        m[ht] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= alpha;
-      }
-
-      // V^T columns from LDS: lane (g, n) takes column 16 dt + n of the
-      // tokens it holds weights for, 16 (j / 4) + 4 g + j % 4
-      const _Float16* vh = reinterpret_cast<const _Float16*>(vb);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        half8_t va;
-        const int chunk = 2 * dt + (n >> 3);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r = 16 * (j >> 2) + 4 * g + (j & 3);
-          va[j] = vh[r * D + ((chunk ^ L::swz(r)) << 3) + (n & 7)];
-        }
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) o[ht][dt] = mfma16x16x32(va, pf[ht], o[ht][dt]);
       }
     }
+    if (nx < nchunks) load_k(kr, nx);
+
+    // online softmax per head column; the weights become the B operand
+    half8_t pf[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      float mloc = sc[ht][0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[ht][j]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float m_new = fmaxf(m[ht], mloc);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m[ht] - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const _Float16 ph = static_cast<_Float16>(fast_exp2(sc[ht][j] - m_use));
+        pf[ht][j] = ph;
+        psum += static_cast<float>(ph);  // the weights the product uses
+      }
+      lsum[ht] = lsum[ht] * alpha + psum;
+      m[ht] = m_new;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= alpha;
+    }
+
+    // V^T tiles by transposing reads: lane (g, n) gets column 16 dt + n of
+    // tokens 16 h + 4 g + k (k = 0..3) from the read of half h
+    const int k4 = n >> 2, q4 = n & 3;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      half8_t va;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int r = 16 * hf + 4 * g + k4;
+        const int chunk = (2 * dt + (q4 >> 1)) ^ L::swz(r);
+        // (bit-cast the whole vector: a bit-cast of one vector element is
+        // lowered as element 0 by this compiler)
+        const half4_t x = __builtin_bit_cast(
+            half4_t, lds_read_tr16(reinterpret_cast<const char*>(vb) + r * (2 * D) + chunk * 16 + (q4 & 1) * 8));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) va[4 * hf + k] = x[k];
+      }
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) o[ht][dt] = mfma16x16x32(va, pf[ht], o[ht][dt]);
+    }
+  };
+
+  {
+    Vec16 kr[2][KLOADS], vr[NV];
+    if (w < nchunks) {
+      load_k(kr, w);
+      load_v(vr, w);
+    }
+    for (int c = w; c < nchunks; c += NW) process_chunk(kr, vr, c, c + NW);
   }
 
   // each head's weight sum over the wave's four lane groups
@@ -381,7 +431,6 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
         const int d = 16 * dt + 4 * g;
         if (nparts == 1) {
           const float f = bad ? NAN : (ctx > 0 ? P.v_scale / lx : 0.f);
-          typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
           half4_t r;
 #pragma unroll
           for (int i = 0; i < 4; ++i) r[i] = static_cast<_Float16>(bad ? NAN : o[ht][dt][i] * f);
@@ -410,20 +459,10 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
     is_last = __hip_atomic_fetch_add(&P.counters[cidx], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
   __syncthreads();
   if (!is_last) return;
-  for (int i = tid; i < nh * D; i += NW * 64) {
-    const int hh = i / D, d = i % D;
-    const int64_t sh = static_cast<int64_t>(s) * P.hq + h0 + hh;
-    const float* ml = P.ws_ml + sh * P.max_parts * 2;
-    float mx = -INFINITY;
-    for (int q = 0; q < nparts; ++q) mx = fmaxf(mx, coherent_load(&ml[2 * q]));
-    float ov = 0.f, lv = 0.f;
-    for (int q = 0; q < nparts; ++q) {
-      const float f = exp2f(coherent_load(&ml[2 * q]) - mx);
-      lv += f * coherent_load(&ml[2 * q + 1]);
-      ov += f * coherent_load(&P.ws_o[(sh * P.max_parts + q) * D + d]);
-    }
-    out[sh * D + d] = static_cast<half_t>(ov / lv);
-  }
+  // the V staging buffers are free now: they hold the merge's scratch
+  float* scratch = reinterpret_cast<float*>(&vbuf[0][0]);
+  merge_partials<half_t, D, NW * 64>(P, static_cast<int64_t>(s) * P.hq + h0, nh, nparts, tid, scratch,
+                                     scratch + kMergeCap);
   if (tid == 0) __hip_atomic_store(&P.counters[cidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -436,12 +475,12 @@ constexpr int max_head_tiles() {
 
 template <typename KV, int D, int HT>
 hipError_t launch_ht(const DecodeArgs& a, int groups) {
-  constexpr int NW = PA_GROUP_WAVES, U = PA_GROUP_UNROLL;
+  constexpr int NW = PA_GROUP_WAVES;
   const DecodeParams P = make_decode_params(a);
   const dim3 grid(static_cast<unsigned>(a.cache->num_kv_heads * groups), static_cast<unsigned>(a.max_parts),
                   static_cast<unsigned>(a.num_seqs));
   if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
-  hipLaunchKernelGGL((decode_group_kernel<KV, D, HT, NW, U>), grid, dim3(NW * 64), 0, a.stream, P, groups);
+  hipLaunchKernelGGL((decode_group_kernel<KV, D, HT, NW>), grid, dim3(NW * 64), 0, a.stream, P, groups);
   const hipError_t e = hipGetLastError();
   if (a.ev[1]) (void)hipEventRecord(a.ev[1], a.stream);
   return e;

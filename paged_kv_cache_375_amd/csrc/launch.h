@@ -13,6 +13,10 @@ namespace pa {
 #define PA_PARTITION_TOKENS 512
 #endif
 constexpr int kPartitionTokens = PA_PARTITION_TOKENS;
+// Partitions one exact merge handles, hence the longest context a decode call
+// accepts: kMaxPartitions * kPartitionTokens tokens.
+constexpr int kMaxPartitions = 1024;
+constexpr int kMaxContextLen = kMaxPartitions * kPartitionTokens;
 
 hipError_t launch_append(const pa_kv_cache& c, const void* k_new, const void* v_new, int act, const int32_t* tables,
                          const int32_t* ctx, int num_seqs, int max_blocks, hipStream_t st);

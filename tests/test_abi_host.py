@@ -68,6 +68,12 @@ def test_decode_argument_checks_fail_before_any_launch():
     assert L.pa_decode_workspace_size(2, 4, 128, 512) == 0  # one partition: no workspace
     # zero sequences: nothing to do, nothing launched
     assert _decode(_cache(), B=0) == _lib.PA_OK
+    # one exact merge handles at most 1024 partitions of 512 tokens
+    big = 1024 * 512
+    need = L.pa_decode_workspace_size(2, 4, 128, big)
+    assert _decode(_cache(), mctx=big, wsb=need, ws=0x7000, B=0) == _lib.PA_OK
+    assert _decode(_cache(), mctx=big + 1, wsb=need * 2, ws=0x7000) == _lib.PA_ERR_UNSUPPORTED
+    assert b"max_context_len" in L.pa_last_error()
 
 
 def test_append_and_copy_argument_checks():
