@@ -14,17 +14,20 @@
 // Computing S transposed puts the weights P^T straight into the B-operand
 // layout of the second product: the lane that holds head n's scores for
 // tokens {4g..4g+3, 16+4g..16+4g+3} (g = lane / 16) is the lane that feeds
-// those tokens into the contraction, so P never moves between lanes.  The
-// head_dim order of the first product's contraction is free (Q and K use the
-// same order), so every K row is read with 16-byte loads straight into the
-// A operand.  V^T needs each lane to hold eight tokens of one head_dim
-// column, so the V rows of a chunk are loaded with coalesced 16-byte loads,
-// written to the wave's slice of LDS (16-byte chunks XOR-swizzled by row so
-// the reads do not collide on banks), and read back with gfx950's transposing
-// LDS read (ds_read_b64_tr_b16: lane i of each 16-lane group receives element
-// i of the four 8-byte rows addressed by lanes 4k..4k+3, k = 0..3), two reads
-// per 16-column tile.  The loop is software-pipelined: the next chunk's K and
-// V loads are in flight while the current chunk is computed.
+// those tokens into the contraction, so P never moves between lanes.
+//
+// The operand layouts put each of 16 consecutive lanes on a different token,
+// which the vector memory path cannot combine, so K and V rows are instead
+// loaded with fully coalesced 16-byte loads (a wave load reads whole rows),
+// converted to f16 if the pool is FP8, and written to the wave's slice of
+// LDS with their 16-byte chunks XOR-swizzled by row.  K is read back as
+// operand rows (ds_read_b128; the head_dim order of the first contraction is
+// free as long as Q uses the same); V, which the second product needs as
+// columns, is read back with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16: lane i of each 16-lane group receives element i of
+// the four 8-byte rows addressed by lanes 4k..4k+3, k = 0..3), two reads per
+// 16-column tile.  The loop is software-pipelined: the next chunk's K and V
+// loads are issued as soon as the current ones are in LDS.
 //
 // Heads past the group (padding up to 16 per tile) have q = 0 and are never
 // written.  The NW wavefronts' partial results are merged in a fixed order
@@ -44,11 +47,16 @@ namespace {
 #ifndef PA_GROUP_WAVES
 #define PA_GROUP_WAVES 4
 #endif
+// Minimum waves per SIMD the register allocation must allow.
+#ifndef PA_GROUP_OCC
+#define PA_GROUP_OCC 2
+#endif
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 32;  // tokens per chunk: two 16-row tiles of the first product
+constexpr float kLazy = 8.f;  // running-max slack, log2 units (weights <= 256)
 
 __device__ __forceinline__ float4_t mfma16x16x32(const half8_t& a, const half8_t& b, const float4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -88,29 +96,24 @@ __device__ __forceinline__ half8_t e4m3x8_to_half8(uint32_t lo, uint32_t hi) {
 template <typename KV, int D>
 struct Layout {
   static constexpr int KVB = Elem<KV>::bytes;
-  static constexpr int NS = D / 32;                  // k-steps of the first product
-  static constexpr int NDT = D / 16;                 // 16-wide head_dim tiles of the second
-  static constexpr bool PAIR = KVB == 1 && NS >= 2;  // FP8: one 16-byte load feeds two k-steps
-  static constexpr int KLOADS = PAIR ? NS / 2 : NS;  // K loads per lane per 16-token tile
-  static constexpr int VCH = D * KVB / 16;           // 16-byte pool chunks per token row
-  static constexpr int NV = kChunk * VCH / 64;       // V loads per lane per chunk
-  static constexpr int LCH = D / 8;                  // 16-byte f16 chunks per LDS row
-  static_assert(NV >= 1 && (kChunk * VCH) % 64 == 0, "head_dim does not fit the V load layout");
-  // first element of the 8 head_dim values lane group g feeds into k-step st
-  static __device__ __forceinline__ int dbase(int st, int g) {
-    return PAIR ? 64 * (st >> 1) + 16 * g + 8 * (st & 1) : 32 * st + 8 * g;
-  }
-  // byte offset within a pool row of the lane group's K load kl
-  static __device__ __forceinline__ int kbyte(int kl, int g) { return PAIR ? 64 * kl + 16 * g : dbase(kl, g) * KVB; }
-  // XOR swizzle of the 16-byte chunks of LDS row r: eight consecutive rows
-  // put any 32-byte column pair in distinct banks (fewer for short rows)
-  static __device__ __forceinline__ int swz(int r) { return (2 * r) & (LCH - 2); }
+  static constexpr int NS = D / 32;             // k-steps of the first product
+  static constexpr int NDT = D / 16;            // 16-wide head_dim tiles of the second
+  static constexpr int VCH = D * KVB / 16;      // 16-byte pool chunks per token row
+  static constexpr int NV = kChunk * VCH / 64;  // loads per lane per chunk, each of K and V
+  static constexpr int LCH = D / 8;             // 16-byte f16 chunks per LDS row
+  static_assert(NV >= 1 && (kChunk * VCH) % 64 == 0, "head_dim does not fit the load layout");
+  // XOR swizzles of the 16-byte chunks of LDS row r.  K rows are read as
+  // operand rows (16 consecutive rows, one chunk each): the row's low bits.
+  // V rows are read by transposing reads (eight rows, a 32-byte column pair
+  // each): twice the row's low bits.  Both keep the reads off shared banks.
+  static __device__ __forceinline__ int swz_k(int r) { return r & (LCH - 1); }
+  static __device__ __forceinline__ int swz_v(int r) { return (2 * r) & (LCH - 2); }
 };
 
-template <typename KV, int D, int HT, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParams P, int groups_per_kv) {
+template <typename KV, int D, int HT, int NW, bool UNI>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROUP_OCC))) void decode_group_kernel(const DecodeParams P, int groups_per_kv) {
   using L = Layout<KV, D>;
-  constexpr int KVB = L::KVB, NS = L::NS, NDT = L::NDT, KLOADS = L::KLOADS, NV = L::NV, LCH = L::LCH;
+  constexpr int KVB = L::KVB, NS = L::NS, NDT = L::NDT, NV = L::NV, LCH = L::LCH;
   constexpr int VCH = L::VCH;
   constexpr int PART = kPartitionTokens;
   constexpr int MREGS = HT * NDT * 4 + 2 * HT;  // floats per lane in a wave's partial result
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
   const int64_t block_rows = static_cast<int64_t>(P.hkv) * bs;
 
   __shared__ int tab[PART];
-  __shared__ uint4 vbuf[NW][kChunk * LCH];  // each wave's V chunk as f16 rows
+  __shared__ uint4 vbuf[NW][kChunk * LCH];  // each wave's K, then V, chunk as f16 rows
   static_assert(sizeof(vbuf) >= 2 * kMergeCap * sizeof(float), "merge scratch does not fit");
   __shared__ float mbuf[MREGS][64];         // one wave's partial result, for the merge
   __shared__ int is_last;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
     for (int st = 0; st < NS; ++st) {
       if (hh < nh) {
         const half_t* qrow = static_cast<const half_t*>(P.q) + (static_cast<int64_t>(s) * P.hq + h0 + hh) * D;
-        qf[ht][st] = as_half8(load16(qrow + L::dbase(st, g)));
+        qf[ht][st] = as_half8(load16(qrow + 32 * st + 8 * g));
       } else {
         qf[ht][st] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
       }
@@ -201,124 +204,120 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
   // the chunk holding the new token (only it needs substitution); -1 if none
   const int new_chunk = has_new ? (ctx - 1 - t0) / kChunk : -1;
 
-  // Pool row (in token rows of the pool) of the lane's token t of chunk c's
-  // 16-token tile tau.  With blocks of 16 or more tokens a tile lies in one
-  // block, so one table entry serves the tile (a wave-uniform read).
-  auto tile_row = [&](int cb, int tau, int t) -> int64_t {
-    const int tt = bs >= 16 ? min(cb + 16 * tau, t1 - 1) : t;
-    return tab[(tt >> log2_bs) - b0] * block_rows + head_rows + (t & (bs - 1));
+  // Addresses.  UNI (blocks of 16 or more tokens): a 16-token tile of a
+  // chunk lies in one block, so each tile's block is one wave-uniform table
+  // read and lanes add 32-bit offsets within the block.  Otherwise every
+  // lane looks up its own token's block.
+  const int64_t tile_bytes = static_cast<int64_t>(bs) * D * KVB;  // one (block, head) tile
+  auto tile_base = [&](const char* pool, int cb, int tau) -> const char* {
+    const int blk = __builtin_amdgcn_readfirstlane(tab[(min(cb + 16 * tau, t1 - 1) >> log2_bs) - b0]);
+    return pool + (static_cast<int64_t>(blk) * P.hkv + kvh) * tile_bytes;
   };
-  // Issue the K loads (the lane's two token rows) and the V loads of chunk
-  // c; the new token's slot is read like any other (its pool value is
-  // replaced when the chunk is consumed).
-  auto load_k = [&](Vec16 (&kr)[2][KLOADS], int c) {
-    const int cb = t0 + c * kChunk;
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int t = min(cb + 16 * tau + n, t1 - 1);
-      const char* rp = P.kc + tile_row(cb, tau, t) * (D * KVB);
-#pragma unroll
-      for (int kl = 0; kl < KLOADS; ++kl) {
-        if constexpr (KVB == 2 || L::PAIR) {
-          kr[tau][kl] = load16_stream(rp + L::kbyte(kl, g));
-        } else {  // FP8, head_dim 32: 8-byte loads
-          const uint2 x = *reinterpret_cast<const uint2*>(rp + L::kbyte(kl, g));
-          kr[tau][kl] = Vec16{{x.x, x.y, 0, 0}};
-        }
+  auto lane_row = [&](const char* pool, int t) -> const char* {
+    return pool + (tab[(t >> log2_bs) - b0] * block_rows + head_rows + (t & (bs - 1))) * (D * KVB);
+  };
+  // Loads of chunk c, coalesced: load v of lane l covers 16 bytes (chunk
+  // ch) of token row r = (64 v + l) / VCH, so a wave load reads whole rows.
+  // K and V rows share the offsets.  The new token's slot is read like any
+  // other; its pool value is replaced when the chunk is consumed.
+  auto row_off = [&](int cb, int v, const char* pool) -> const char* {
+    const int f = v * 64 + lane;
+    const int r = f / VCH, ch = f % VCH;
+    const int t = min(cb + r, t1 - 1);
+    if constexpr (UNI) {
+      // rows per load are 64 / VCH: a load stays within one 16-token tile
+      // when that is at most 16, so its tile is known at compile time;
+      // otherwise (32 rows per load) each lane picks one of the two bases
+      const char* base;
+      if constexpr (64 / VCH <= 16) {
+        base = tile_base(pool, cb, (v * (64 / VCH)) >> 4);
+      } else {
+        const char* b0p = tile_base(pool, cb, 0);
+        const char* b1p = tile_base(pool, cb, 1);
+        base = (r >> 4) ? b1p : b0p;
       }
+      return base + (t & (bs - 1)) * (D * KVB) + ch * 16;
+    } else {
+      return lane_row(pool, t) + ch * 16;
     }
   };
-  auto load_v = [&](Vec16 (&vr)[NV], int c) {
+  auto load_rows = [&](Vec16 (&x)[NV], const char* pool, int c) {
+    const int cb = t0 + c * kChunk;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) x[v] = load16_stream(row_off(cb, v, pool));
+  };
+  // The chunk holding the new token: lanes at its row (and lanes past the
+  // context, which re-read it) take the caller's K/V in pool format, staged
+  // in LDS at the start.
+  auto substitute = [&](Vec16 (&x)[NV], int which, int c) {
     const int cb = t0 + c * kChunk;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int f = v * 64 + lane;
       const int r = f / VCH, ch = f % VCH;
-      const int t = min(cb + r, t1 - 1);
-      vr[v] = load16_stream(P.vc + tile_row(cb, r >> 4, t) * (D * KVB) + ch * 16);
+      if (min(cb + r, t1 - 1) == ctx - 1) x[v] = newkv[which][ch];
     }
   };
-  // The chunk holding the new token: lanes at its position (and lanes past
-  // the context, which re-read it) take the caller's K/V in pool format,
-  // staged in LDS at the start.
-  auto substitute = [&](Vec16 (&kr)[2][KLOADS], Vec16 (&vr)[NV], int c) {
-    const int cb = t0 + c * kChunk;
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      if (min(cb + 16 * tau + n, t1 - 1) != ctx - 1) continue;
-#pragma unroll
-      for (int kl = 0; kl < KLOADS; ++kl) {
-        if constexpr (KVB == 2 || L::PAIR) {
-          kr[tau][kl] = newkv[0][L::kbyte(kl, g) / 16];
-        } else {  // 8-byte K pieces
-          const Vec16 cn = newkv[0][g >> 1];
-          kr[tau][kl] = Vec16{{cn.w[2 * (g & 1)], cn.w[2 * (g & 1) + 1], 0, 0}};
-        }
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int f = v * 64 + lane;
-      const int r = f / VCH, ch = f % VCH;
-      if (min(cb + r, t1 - 1) == ctx - 1) vr[v] = newkv[1][ch];
-    }
-  };
-
-  // Compute chunk c from its loaded K and V; the registers are refilled with
-  // chunk nx's loads as soon as they are consumed (V once it is in LDS, K once
-  // the score products have read it), so those loads fly during the rest.
-  auto process_chunk = [&](Vec16 (&kr)[2][KLOADS], Vec16 (&vr)[NV], int c, int nx) {
-    const int cb = t0 + c * kChunk;
-    if (c == new_chunk) substitute(kr, vr, c);  // wave-uniform, at most once
-    // V rows into the wave's LDS slice as f16 (the previous chunk's reads
-    // were issued before these writes; one wave's LDS accesses complete in
-    // order)
+  // Rows of a chunk into the wave's LDS slice as f16 (FP8 converted
+  // exactly), 16-byte chunks swizzled by swz(row).
+  auto rows_to_lds = [&](const Vec16 (&x)[NV], auto swz) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int f = v * 64 + lane;
       const int r = f / VCH, ch = f % VCH;
       if constexpr (KVB == 2) {
-        vb[r * LCH + (ch ^ L::swz(r))] = make_uint4(vr[v].w[0], vr[v].w[1], vr[v].w[2], vr[v].w[3]);
+        vb[r * LCH + (ch ^ swz(r))] = make_uint4(x[v].w[0], x[v].w[1], x[v].w[2], x[v].w[3]);
       } else {
-        const half8_t a = e4m3x8_to_half8(vr[v].w[0], vr[v].w[1]);
-        const half8_t b = e4m3x8_to_half8(vr[v].w[2], vr[v].w[3]);
-        vb[r * LCH + ((2 * ch) ^ L::swz(r))] = __builtin_bit_cast(uint4, a);
-        vb[r * LCH + ((2 * ch + 1) ^ L::swz(r))] = __builtin_bit_cast(uint4, b);
+        const half8_t lo = e4m3x8_to_half8(x[v].w[0], x[v].w[1]);
+        const half8_t hi = e4m3x8_to_half8(x[v].w[2], x[v].w[3]);
+        vb[r * LCH + ((2 * ch) ^ swz(r))] = __builtin_bit_cast(uint4, lo);
+        vb[r * LCH + ((2 * ch + 1) ^ swz(r))] = __builtin_bit_cast(uint4, hi);
       }
     }
-    if (nx < nchunks) load_v(vr, nx);
+  };
+
+  // Compute chunk c from its loaded K and V.  The register copies are
+  // refilled with chunk nx's loads as soon as they are in LDS, so those loads
+  // fly during the rest of the chunk.  One wave's LDS accesses complete in
+  // order, so the V rows may overwrite the K rows once the K reads are issued.
+  auto process_chunk = [&](Vec16 (&kr)[NV], Vec16 (&vr)[NV], int c, int nx) {
+    const int cb = t0 + c * kChunk;
+    const bool sub = c == new_chunk;  // wave-uniform, at most once
+    if (sub) substitute(kr, 0, c);
+    rows_to_lds(kr, L::swz_k);
+    if (nx < nchunks) load_rows(kr, P.kc, nx);
 
     // scores S^T: lane (g, n) gets tokens 16 tau + 4 g + i of head 16 ht + n
     float sc[HT][8];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
+      const int r = 16 * tau + n;
       half8_t ka[NS];
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        if constexpr (KVB == 2) {
-          ka[st] = as_half8(kr[tau][st]);
-        } else if constexpr (L::PAIR) {
-          const Vec16& x = kr[tau][st >> 1];
-          ka[st] = (st & 1) ? e4m3x8_to_half8(x.w[2], x.w[3]) : e4m3x8_to_half8(x.w[0], x.w[1]);
-        } else {
-          ka[st] = e4m3x8_to_half8(kr[tau][st].w[0], kr[tau][st].w[1]);
-        }
-      }
+      for (int st = 0; st < NS; ++st) ka[st] = __builtin_bit_cast(half8_t, vb[r * LCH + ((4 * st + g) ^ L::swz_k(r))]);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < NS; ++st) acc = mfma16x16x32(ka[st], qf[ht][st], acc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = cb + 16 * tau + 4 * g + i;
-          sc[ht][4 * tau + i] = tok < t1 ? acc[i] * P.score_scale : -INFINITY;
+        for (int i = 0; i < 4; ++i) sc[ht][4 * tau + i] = acc[i] * P.score_scale;
+        if (cb + kChunk > t1) {  // the partition's last chunk: mask tokens past its end
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (cb + 16 * tau + 4 * g + i >= t1) sc[ht][4 * tau + i] = -INFINITY;
         }
       }
     }
-    if (nx < nchunks) load_k(kr, nx);
 
-    // online softmax per head column; the weights become the B operand
+    if (sub) substitute(vr, 1, c);
+    rows_to_lds(vr, L::swz_v);
+    if (nx < nchunks) load_rows(vr, P.vc, nx);
+
+    // online softmax per head column; the weights become the B operand.
+    // The running max moves only when a chunk's max exceeds it by more than
+    // kLazy (log2 units), so weights stay at most 2^kLazy and the rescale of
+    // the accumulators is skipped by the whole wave in most chunks.
     half8_t pf[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -327,20 +326,23 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
       for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[ht][j]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m[ht], mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m[ht] - m_use);
+      const bool raise = mloc > m[ht] + kLazy;  // uniform within a head column
+      if (__any(raise)) {
+        const float m_new = raise ? mloc : m[ht];
+        const float alpha = fast_exp2(m[ht] - m_new);  // 0 on the first chunk (m = -inf)
+        lsum[ht] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= alpha;
+        m[ht] = m_new;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const _Float16 ph = static_cast<_Float16>(fast_exp2(sc[ht][j] - m_use));
+        const _Float16 ph = static_cast<_Float16>(fast_exp2(sc[ht][j] - m[ht]));
         pf[ht][j] = ph;
         psum += static_cast<float>(ph);  // the weights the product uses
       }
-      lsum[ht] = lsum[ht] * alpha + psum;
-      m[ht] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= alpha;
+      lsum[ht] += psum;
     }
 
     // V^T tiles by transposing reads: lane (g, n) gets column 16 dt + n of
@@ -352,7 +354,7 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int r = 16 * hf + 4 * g + k4;
-        const int chunk = (2 * dt + (q4 >> 1)) ^ L::swz(r);
+        const int chunk = (2 * dt + (q4 >> 1)) ^ L::swz_v(r);
         // (bit-cast the whole vector: a bit-cast of one vector element is
         // lowered as element 0 by this compiler)
         const half4_t x = __builtin_bit_cast(
@@ -366,10 +368,10 @@ __global__ __launch_bounds__(NW * 64) void decode_group_kernel(const DecodeParam
   };
 
   {
-    Vec16 kr[2][KLOADS], vr[NV];
+    Vec16 kr[NV], vr[NV];
     if (w < nchunks) {
-      load_k(kr, w);
-      load_v(vr, w);
+      load_rows(kr, P.kc, w);
+      load_rows(vr, P.vc, w);
     }
     for (int c = w; c < nchunks; c += NW) process_chunk(kr, vr, c, c + NW);
   }
@@ -479,8 +481,10 @@ hipError_t launch_ht(const DecodeArgs& a, int groups) {
   const DecodeParams P = make_decode_params(a);
   const dim3 grid(static_cast<unsigned>(a.cache->num_kv_heads * groups), static_cast<unsigned>(a.max_parts),
                   static_cast<unsigned>(a.num_seqs));
+  auto kern = a.cache->block_size >= 16 ? decode_group_kernel<KV, D, HT, NW, true>
+                                        : decode_group_kernel<KV, D, HT, NW, false>;
   if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
-  hipLaunchKernelGGL((decode_group_kernel<KV, D, HT, NW>), grid, dim3(NW * 64), 0, a.stream, P, groups);
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, a.stream, P, groups);
   const hipError_t e = hipGetLastError();
   if (a.ev[1]) (void)hipEventRecord(a.ev[1], a.stream);
   return e;
