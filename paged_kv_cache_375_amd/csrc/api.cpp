@@ -3,6 +3,9 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -123,6 +126,26 @@ extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads
   return counters_bytes(num_seqs, num_q_heads) +
          static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
 }
+
+namespace pa {
+
+int resident_slots(const void* kernel, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({kernel, dev});
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess) return 0;
+  const int n = cus * (per > 0 ? per : 1);
+  cache[{kernel, dev}] = n;
+  return n;
+}
+
+}  // namespace pa
 
 namespace {
 

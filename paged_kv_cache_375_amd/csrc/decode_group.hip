@@ -4,7 +4,9 @@
 // cores (v_mfma_f32_16x16x32_f16, f32 accumulation).
 //
 // One workgroup per (KV head and group of up to 16 * HT query heads,
-// partition of kPartitionTokens tokens, sequence).  Its NW wavefronts take
+// partition, sequence).  The partition length is chosen per launch (a
+// multiple of kPartitionTokens): the shortest whose workgroups all fit on the
+// GPU at once, else kPartitionTokens.  Its NW wavefronts take
 // 32-token chunks of the partition in turn; a chunk is processed as
 //
 //   S^T[32 tokens][16 heads] = K[32][D] . Q^T[D][16]      (2 x D/32 MFMAs per head tile)
@@ -47,10 +49,12 @@ namespace {
 #ifndef PA_GROUP_WAVES
 #define PA_GROUP_WAVES 4
 #endif
-// Minimum waves per SIMD the register allocation must allow.
-#ifndef PA_GROUP_OCC
-#define PA_GROUP_OCC 2
-#endif
+// Minimum waves per SIMD the register allocation must allow: three where
+// the head tiles fit without spilling, else two.
+template <int D, int HT>
+constexpr int group_occupancy() {
+  return D >= 128 || (D == 64 && HT >= 3) ? 2 : 3;
+}
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -111,11 +115,10 @@ struct Layout {
 };
 
 template <typename KV, int D, int HT, int NW, bool UNI>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROUP_OCC))) void decode_group_kernel(const DecodeParams P, int groups_per_kv) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_occupancy<D, HT>()))) void decode_group_kernel(const DecodeParams P, int groups_per_kv) {
   using L = Layout<KV, D>;
   constexpr int KVB = L::KVB, NS = L::NS, NDT = L::NDT, NV = L::NV, LCH = L::LCH;
   constexpr int VCH = L::VCH;
-  constexpr int PART = kPartitionTokens;
   constexpr int MREGS = HT * NDT * 4 + 2 * HT;  // floats per lane in a wave's partial result
 
   const int grp = blockIdx.x % groups_per_kv;
@@ -130,10 +133,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROU
   const int ctx = P.ctx[s];
   const bool bad_len =
       ctx < 0 || ctx > P.max_ctx || static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) * bs;
-  const int nparts = bad_len ? 1 : max(1, (ctx + PART - 1) / PART);
+  const int part = P.part_tokens;  // a multiple of kPartitionTokens, chosen per launch
+  const int nparts = bad_len ? 1 : max(1, (ctx + part - 1) / part);
   if (p >= nparts) return;
-  const int t0 = p * PART;
-  const int t1 = bad_len ? t0 : min(t0 + PART, ctx);
+  const int t0 = p * part;
+  const int t1 = bad_len ? t0 : min(t0 + part, ctx);
   const int b0 = t0 >> log2_bs;
   const int64_t trow = static_cast<int64_t>(s) * P.max_blocks;
   const int h0 = kvh * P.group + grp * HT * 16;              // first query head of the workgroup
@@ -141,12 +145,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROU
   const int64_t head_rows = static_cast<int64_t>(kvh) * bs;  // token rows before head kvh in a block
   const int64_t block_rows = static_cast<int64_t>(P.hkv) * bs;
 
-  __shared__ int tab[PART];
-  __shared__ uint4 vbuf[NW][kChunk * LCH];  // each wave's K, then V, chunk as f16 rows
-  static_assert(sizeof(vbuf) >= 2 * kMergeCap * sizeof(float), "merge scratch does not fit");
+  __shared__ int tab[kTabEntries];  // the partition's table slice (part / block_size entries)
+  // each wave's K, then V, chunk as f16 rows; afterwards the merge's scratch
+  constexpr int kVbuf = NW * kChunk * LCH > kMergeCap / 2 ? NW * kChunk * LCH : kMergeCap / 2;
+  __shared__ uint4 vbuf[kVbuf];
   __shared__ float mbuf[MREGS][64];         // one wave's partial result, for the merge
   __shared__ int is_last;
   __shared__ Vec16 newkv[2][VCH];  // the new token's K and V rows in pool format
+  __shared__ uint4 qs[HT * 16 * LCH];  // the workgroup's q rows (f16), zero past the group
 
   int my_bad = bad_len ? 1 : 0;
   {
@@ -165,6 +171,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROU
   // from the caller's rows instead of the pool.
   const bool has_new = P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
   if (has_new && grp == 0 && w == 0) store_new_token<KV, half_t, D>(P, s, kvh, ctx, lane);
+  for (int i = tid; i < HT * 16 * LCH; i += NW * 64) {
+    const int hh = i / LCH, ch = i % LCH;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (hh < nh) x = *reinterpret_cast<const uint4*>(static_cast<const half_t*>(P.q) +
+                                                     (static_cast<int64_t>(s) * P.hq + h0 + hh) * D + ch * 8);
+    qs[hh * LCH + (ch ^ L::swz_k(hh))] = x;
+  }
   if (has_new && tid < 2 * VCH) {
     const int64_t src = (static_cast<int64_t>(s) * P.hkv + kvh) * D * static_cast<int64_t>(sizeof(half_t));
     const int which = tid / VCH, ch = tid % VCH;
@@ -172,22 +185,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROU
   }
   const bool bad = __syncthreads_or(my_bad) != 0;
 
-  // B operand of the first product: q of head 16 * ht + n at the head_dim
-  // positions lane group g feeds into each k-step (zero past the group)
-  half8_t qf[HT][NS];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
+  // B operand of the first product: q of head 16 * ht + n at head_dim
+  // 32 st + 8 g .. + 7, read per chunk from the workgroup's copy of q in LDS
+  // (rows swizzled like K's; zero past the group)
+  auto q_operand = [&](int ht, int st) -> half8_t {
     const int hh = 16 * ht + n;
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      if (hh < nh) {
-        const half_t* qrow = static_cast<const half_t*>(P.q) + (static_cast<int64_t>(s) * P.hq + h0 + hh) * D;
-        qf[ht][st] = as_half8(load16(qrow + 32 * st + 8 * g));
-      } else {
-        qf[ht][st] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-  }
+    return __builtin_bit_cast(half8_t, qs[hh * LCH + ((4 * st + g) ^ L::swz_k(hh))]);
+  };
 
   float4_t o[HT][NDT];
   float m[HT], lsum[HT];
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROU
     for (int dt = 0; dt < NDT; ++dt) o[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  uint4* const vb = vbuf[w];
+  uint4* const vb = vbuf + w * (kChunk * LCH);
   const int nchunks = bad ? 0 : (t1 - t0 + kChunk - 1) / kChunk;
   // the chunk holding the new token (only it needs substitution); -1 if none
   const int new_chunk = has_new ? (ctx - 1 - t0) / kChunk : -1;
@@ -236,7 +240,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROU
         const char* b1p = tile_base(pool, cb, 1);
         base = (r >> 4) ? b1p : b0p;
       }
-      return base + (t & (bs - 1)) * (D * KVB) + ch * 16;
+      // an unsigned 32-bit offset lets the load take the scalar base as is
+      return base + static_cast<uint32_t>((t & (bs - 1)) * (D * KVB) + ch * 16);
     } else {
       return lane_row(pool, t) + ch * 16;
     }
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROU
       for (int ht = 0; ht < HT; ++ht) {
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < NS; ++st) acc = mfma16x16x32(ka[st], qf[ht][st], acc);
+        for (int st = 0; st < NS; ++st) acc = mfma16x16x32(ka[st], q_operand(ht, st), acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[ht][4 * tau + i] = acc[i] * P.score_scale;
         if (cb + kChunk > t1) {  // the partition's last chunk: mask tokens past its end
@@ -462,7 +467,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(PA_GROU
   __syncthreads();
   if (!is_last) return;
   // the V staging buffers are free now: they hold the merge's scratch
-  float* scratch = reinterpret_cast<float*>(&vbuf[0][0]);
+  float* scratch = reinterpret_cast<float*>(vbuf);
   merge_partials<half_t, D, NW * 64>(P, static_cast<int64_t>(s) * P.hq + h0, nh, nparts, tid, scratch,
                                      scratch + kMergeCap);
   if (tid == 0) __hip_atomic_store(&P.counters[cidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -478,11 +483,30 @@ constexpr int max_head_tiles() {
 template <typename KV, int D, int HT>
 hipError_t launch_ht(const DecodeArgs& a, int groups) {
   constexpr int NW = PA_GROUP_WAVES;
-  const DecodeParams P = make_decode_params(a);
-  const dim3 grid(static_cast<unsigned>(a.cache->num_kv_heads * groups), static_cast<unsigned>(a.max_parts),
-                  static_cast<unsigned>(a.num_seqs));
   auto kern = a.cache->block_size >= 16 ? decode_group_kernel<KV, D, HT, NW, true>
                                         : decode_group_kernel<KV, D, HT, NW, false>;
+  // Partition length: the shortest multiple of kPartitionTokens (doubling)
+  // whose worst-case workgroup count fits the GPU's resident slots, so the
+  // whole launch runs as one round; when even one partition per unit does
+  // not fit, many short partitions balance best.  Bounded by the LDS table
+  // slice (kTabEntries entries).
+  const int64_t units = static_cast<int64_t>(a.cache->num_kv_heads) * groups * a.num_seqs;
+  const int slots = resident_slots(reinterpret_cast<const void*>(kern), NW * 64);
+  const int64_t cap = static_cast<int64_t>(kTabEntries) * a.cache->block_size;
+  int part = kPartitionTokens;
+  for (int64_t pp = kPartitionTokens; pp <= cap; pp *= 2) {
+    const int64_t parts = (a.max_ctx + pp - 1) / pp;
+    if (units * (parts > 0 ? parts : 1) <= slots) {
+      part = static_cast<int>(pp);
+      break;
+    }
+    if (pp >= a.max_ctx) break;
+  }
+  DecodeParams P = make_decode_params(a);
+  P.part_tokens = part;
+  const int grid_parts = a.max_ctx <= 0 ? 1 : (a.max_ctx + part - 1) / part;
+  const dim3 grid(static_cast<unsigned>(a.cache->num_kv_heads * groups), static_cast<unsigned>(grid_parts),
+                  static_cast<unsigned>(a.num_seqs));
   if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, a.stream, P, groups);
   const hipError_t e = hipGetLastError();

@@ -47,6 +47,15 @@ struct DecodeArgs {
   hipEvent_t ev[2];  // optional timing events around the kernel (or null)
 };
 
+// Table entries a decode workgroup stages in LDS: a partition spans at most
+// kTabEntries blocks.
+constexpr int kTabEntries = 1024;
+
+// Workgroups of `threads` threads of `kernel` the current device holds at
+// once (compute units x workgroups per unit; cached per kernel and device);
+// 0 if the device cannot be queried.
+int resident_slots(const void* kernel, int threads);
+
 // Returns hipErrorInvalidValue for an unsupported dtype/shape combination.
 hipError_t launch_decode(const DecodeArgs& a);
 

@@ -56,6 +56,22 @@ def test_group_kernel_parity(case, fused):
     assert np.array_equal(out, out2)  # deterministic, counters left at zero
 
 
+def test_group_kernel_long_partitions():
+    """64 sequences x 8 KV heads fill the GPU's resident workgroups in one
+    round only with partitions longer than 512 tokens, so the launch picks
+    longer ones; contexts are short and ragged."""
+    wl = Workload("group_64x8_long_part", 64, 8, 128, 16, 64, 1, 1300)
+    print(f"[group] {wl}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    out = out_f64(gpu.run())
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    err = float(np.max(np.abs(out - ref.decode())))
+    print(f"[group] {wl.name}: max abs err {err:.3e}", flush=True)
+    assert err <= TOL["f16"]
+
+
 def test_group_kernel_placement_invariance_bit_exact():
     wl = _wl(64, 8, 128, "f16", 16)
     dr, gpu, ref = build_pair(wl)
