@@ -39,6 +39,14 @@ def workload_label(wl):
             + (f" after a shared {wl.prefix_len}-token prefix" if wl.prefix_len else ""))
 
 
+def decode_kernel_name(wl):
+    """The decode kernel that serves the workload (matrix cores when query
+    heads share KV heads and activations are f16, else the per-head kernel)."""
+    if wl.num_q_heads > wl.num_kv_heads and wl.act == "f16":
+        return "decode_group_kernel (grouped heads on MFMA: append + split-context attention + merge)"
+    return "decode_kernel (per head on VALU: append + split-context attention + merge)"
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_375_amd", "csrc")
@@ -89,7 +97,7 @@ def main():
     ap.add_argument("--block-size", type=int, default=0, help="override the workload's block size")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=0, help="pool copies to rotate over (0: enough for >= 2 GB)")
-    ap.add_argument("--cpu-repeats", type=int, default=2, help="CPU reference runs (0 skips the CPU baseline)")
+    ap.add_argument("--cpu-repeats", type=int, default=4, help="CPU reference runs (0 skips the CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters) and exit")
     args = ap.parse_args()
@@ -206,7 +214,7 @@ def main():
                                 "max": max(sample_ms), "n": n_samples},
         "kernels_ms": {"decode_avg": part_avg_ms, "decode_launches": n_part},
         "wall_s_timed_region": wall,
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel (append + split-context attention + merge)",
+        "roofline": {"bound": "hbm", "kernel": decode_kernel_name(wl),
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
