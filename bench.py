@@ -88,6 +88,64 @@ def cpu_baseline(dr, repeats):
             "cpu": platform.processor() or platform.machine()}
 
 
+def _time_ms(fn, reps):
+    """Mean milliseconds of fn() over reps calls, between HIP events on the current stream."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def bench_writers(wl, dr, step, args):
+    """Throughput of the pool writers over algorithmic bytes (each element read
+    from the source once and written to the pool once)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_375_amd import api
+    from paged_kv_cache_375_amd.accounting import ELEM_BYTES
+
+    ea, ek = ELEM_BYTES[wl.act], ELEM_BYTES[wl.kv]
+    hkv, d, B = wl.num_kv_heads, wl.head_dim, wl.batch
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    k_hist, v_hist = dev(dr.k_hist), dev(dr.v_hist)
+    rows = int(dr.hist_count.sum())
+    tables, hist_row = dev(step.scenario.hist_tables), dev(dr.hist_row)
+    start, count = dev(dr.hist_start), dev(dr.hist_count)
+    mc = int(dr.hist_count.max())
+    lines = []
+
+    ms = _time_ms(lambda: api.kv_write_prompt(step.cache, k_hist, v_hist, hist_row, start, count, tables, mc), 10)
+    nbytes = rows * hkv * d * (ea + ek) * 2 + 16 * B
+    lines.append(("pa_kv_write_prompt", ms, nbytes, f"{rows} history tokens of {B} sequences"))
+
+    ms = _time_ms(lambda: api.kv_append(step.cache, step.k_new, step.v_new, step.tables, step.ctx), 200)
+    nbytes = B * hkv * d * (ea + ek) * 2 + 8 * B
+    lines.append(("pa_kv_append", ms, nbytes, f"one token of each of {B} sequences"))
+
+    n = min(1024, dr.num_blocks // 2)
+    rng = np.random.default_rng(args.seed)
+    perm = rng.permutation(dr.num_blocks).astype(np.int32)
+    pairs = dev(np.stack([perm[:n], perm[n:2 * n]], axis=1))
+    ms = _time_ms(lambda: api.copy_blocks(step.cache, pairs), 20)
+    nbytes = n * 2 * hkv * wl.block_size * d * ek * 2 + 8 * n
+    lines.append(("pa_copy_blocks", ms, nbytes, f"{n} random block pairs"))
+
+    for name, ms, nbytes, what in lines:
+        gbps = nbytes / (ms / 1e3) / 1e9
+        print(json.dumps({"metric": f"{name} HBM GB/s (algorithmic bytes), 1 GPU", "value": gbps, "unit": "GB/s",
+                          "n_gpus": 1, "ms_per_call": ms, "algorithmic_bytes": nbytes, "frac_of_peak":
+                          gbps / HBM_PEAK_GBPS, "config": {"workload": workload_label(wl), "call": what},
+                          "higher_is_better": True, "data": "synthetic"}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,6 +158,9 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=4, help="CPU reference runs (0 skips the CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters) and exit")
+    ap.add_argument("--writers", action="store_true",
+                    help="instead of the decode step, time the pool writers (prompt write, append, block copy) "
+                         "and print one JSON line per writer")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -131,6 +192,9 @@ def main():
     print(f"bench: building {wl.name}", file=sys.stderr, flush=True)
     dr = draw(wl, args.seed)
     step = DecodeStep(dr, "cuda")
+    if args.writers:
+        bench_writers(wl, dr, step, args)
+        return
     sc = step.scenario
     sb = step_bytes(sc.ctx, sc.tables, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.act, wl.kv,
                     len(sc.step_pairs))
