@@ -32,10 +32,13 @@
 namespace pa {
 namespace {
 
-// Launch shape: wavefronts per workgroup and wave loads per batch.
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 4
-#endif
+// Launch shape: wavefronts per workgroup (measured best: eight for f16 and
+// f32 pools, two for FP8 pools, whose lanes do more arithmetic per byte) and
+// wave loads per batch.
+template <typename KV>
+constexpr int decode_waves() {
+  return Elem<KV>::bytes == 1 ? 2 : 8;
+}
 #ifndef PA_DECODE_UNROLL
 #define PA_DECODE_UNROLL 8
 #endif
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
 
 template <typename KV, typename ACT, int D>
 hipError_t decode_t(const DecodeArgs& a) {
-  constexpr int NW = PA_DECODE_WAVES, U = PA_DECODE_UNROLL;
+  constexpr int NW = decode_waves<KV>(), U = PA_DECODE_UNROLL;
   constexpr int TPL = 64 / (D / Math<KV, ACT>::EPL);
   const pa_kv_cache& c = *a.cache;
   const DecodeParams P = make_decode_params(a);
