@@ -146,6 +146,48 @@ def bench_writers(wl, dr, step, args):
                           "higher_is_better": True, "data": "synthetic"}))
 
 
+def bench_swap(wl, args):
+    """Preemption by swapping: host-link GB/s of pa_swap_blocks moving random
+    blocks out to pinned host memory and back, for each block size, beside a
+    plain DMA copy of the same bytes between one device buffer and one pinned
+    host buffer (the link's ceiling for this amount)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_375_amd import api
+    from paged_kv_cache_375_amd.accounting import ELEM_BYTES
+
+    ek = ELEM_BYTES[wl.kv]
+    total = 256 << 20  # K + V bytes moved per call
+    for bs in (1, 2, 4, 8, 16, 32, 64):
+        block = wl.num_kv_heads * bs * wl.head_dim * ek
+        n = total // (2 * block)
+        nb = 2 * n
+        cache = api.KVCache(nb, bs, wl.num_kv_heads, wl.head_dim, wl.kv, "cuda")
+        cache.k.view(torch.uint8).random_(0, 256)
+        cache.v.view(torch.uint8).random_(0, 256)
+        ids = torch.from_numpy(np.random.default_rng(args.seed).permutation(nb)[:n].astype(np.int32)).cuda()
+        hk = torch.empty((n, wl.num_kv_heads, bs, wl.head_dim), dtype=cache.k.dtype).pin_memory()
+        hv = torch.empty_like(hk).pin_memory()
+        nbytes = 2 * n * block
+        for direction in ("out", "in"):
+            ms = _time_ms(lambda: api.swap_blocks(cache, hk, hv, ids, direction), 5)
+            print(json.dumps({"metric": f"pa_swap_blocks host-link GB/s (swap-{direction}), 1 GPU",
+                              "value": nbytes / (ms / 1e3) / 1e9, "unit": "GB/s", "n_gpus": 1, "ms_per_call": ms,
+                              "bytes": nbytes, "config": {"workload": workload_label(wl), "block_size": bs,
+                                                          "blocks": int(n), "block_bytes_k_plus_v": 2 * block},
+                              "higher_is_better": True, "data": "synthetic"}), flush=True)
+        del cache, hk, hv
+    dev = torch.empty(total, dtype=torch.uint8, device="cuda")
+    host = torch.empty(total, dtype=torch.uint8).pin_memory()
+    for direction, fn in (("out", lambda: host.copy_(dev, non_blocking=True)),
+                          ("in", lambda: dev.copy_(host, non_blocking=True))):
+        ms = _time_ms(fn, 5)
+        print(json.dumps({"metric": f"contiguous DMA copy host-link GB/s ({direction}), 1 GPU",
+                          "value": total / (ms / 1e3) / 1e9, "unit": "GB/s", "n_gpus": 1, "ms_per_call": ms,
+                          "bytes": total, "higher_is_better": True, "data": "synthetic"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +203,9 @@ def main():
     ap.add_argument("--writers", action="store_true",
                     help="instead of the decode step, time the pool writers (prompt write, append, block copy) "
                          "and print one JSON line per writer")
+    ap.add_argument("--swap", action="store_true",
+                    help="instead of the decode step, time block swaps to pinned host memory and back for each "
+                         "block size (the workload's heads, head_dim and pool dtype)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -189,6 +234,9 @@ def main():
     wl = WORKLOADS[args.workload]
     if args.block_size:
         wl = wl.with_block_size(args.block_size)
+    if args.swap:
+        bench_swap(wl, args)
+        return
     print(f"bench: building {wl.name}", file=sys.stderr, flush=True)
     dr = draw(wl, args.seed)
     step = DecodeStep(dr, "cuda")

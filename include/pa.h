@@ -136,6 +136,27 @@ pa_status pa_kv_write_prompt(const pa_kv_cache* cache, const void* k_src, const 
 pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst_pairs, int32_t n, void* stream);
 
 /*
+ * pa_swap_blocks — the copy of preemption by swapping: a preempted
+ * sequence's blocks are moved to host memory and moved back when it resumes
+ * [F55 §放不下的时候] (see pa_seq_swap_out / pa_seq_swap_in).
+ *
+ * host_k, host_v: host memory the device can access (pinned, e.g.
+ * hipHostMalloc), each [n][num_kv_heads][block_size][head_dim] of the pool
+ * dtype; entry i holds block block_ids[i].  block_ids: device int32 [n].
+ * direction PA_SWAP_OUT copies pool -> host, PA_SWAP_IN host -> pool; every KV
+ * head and slot, K and V, bit-exact.  The kernel moves 16-byte chunks over
+ * the host link directly, so small blocks cost no more per byte than large
+ * ones.  Ids outside [0, num_blocks) are skipped; swap-in targets must be
+ * distinct.  Host buffers the runtime does not know as pinned give
+ * PA_ERR_INVALID_ARGUMENT before any launch.  Asynchronous on `stream`: the
+ * host buffers must stay allocated, and untouched by the host, until it
+ * completes.
+ */
+typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_direction;
+pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, const int32_t* block_ids, int32_t n,
+                         int32_t direction, void* stream);
+
+/*
  * pa_decode_workspace_size — bytes of device workspace pa_decode and
  * pa_decode_step need for split-context partial results: an int32 arrival
  * counter per (sequence, query head), padded to 256 bytes, then fp32
@@ -241,8 +262,28 @@ pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child);
 /* Reserve the slot of one more token.  *cow_src / *cow_dst receive the block
  * copy the caller must perform (pa_copy_blocks) before writing, or -1 / -1. */
 pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* cow_src, int32_t* cow_dst);
-/* Release the sequence: reference counts - 1, unreferenced blocks are freed. */
+/* Release the sequence: reference counts - 1, unreferenced blocks are freed
+ * (a swapped-out sequence is simply forgotten). */
 pa_status pa_seq_free(pa_allocator* a, int32_t seq);
+/*
+ * Preemption by swapping: when blocks run out, the latest arrival gives up
+ * all of its blocks, which may be moved to host memory and moved back when
+ * it resumes [F55 §放不下的时候].
+ * pa_seq_swap_out releases every block of a resident sequence (reference
+ * counts - 1, unreferenced blocks join the free list; shared blocks stay with
+ * their other holders) and keeps its context length; block_ids (host, room
+ * for cap entries) receives its former blocks in logical order, whose K/V the
+ * caller copies out with pa_swap_blocks(PA_SWAP_OUT) before any later write
+ * can reuse them (issuing the copy first on the same stream suffices).
+ * pa_seq_swap_in takes ceil(ctx / block_size) fresh blocks, all or none
+ * (PA_ERR_OUT_OF_BLOCKS changes nothing), and returns them in logical order
+ * for pa_swap_blocks(PA_SWAP_IN).  Both set *num_blocks to the number of
+ * blocks and fail with PA_ERR_INVALID_ARGUMENT, changing nothing, when cap is
+ * smaller.  A swapped-out sequence keeps its place in arrival order but is
+ * not a preemption candidate; pa_seq_get, append and fork do not see it.
+ */
+pa_status pa_seq_swap_out(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap, int32_t* num_blocks);
+pa_status pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap, int32_t* num_blocks);
 /* Copy the table (up to cap entries) and report its length and context. */
 pa_status pa_seq_get(const pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
                      int32_t* num_blocks, int32_t* context_len);
@@ -252,7 +293,7 @@ pa_status pa_export_tables(const pa_allocator* a, const int32_t* seqs, int32_t n
 int32_t pa_block_refcount(const pa_allocator* a, int32_t block);
 pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out);
 /* The sequence to preempt first when blocks run out: the latest arrival
- * [F55 §放不下的时候]; -1 if none. */
+ * among those holding blocks [F55 §放不下的时候]; -1 if none. */
 int32_t pa_latest_arrival(const pa_allocator* a);
 
 /* ================================ utilities ================================ */

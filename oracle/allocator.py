@@ -10,6 +10,12 @@ The rules, in the pages' words restated:
     blocks or none [F55 §放不下的时候].  Here: a request that cannot be met
     whole changes nothing.
   * A finished sequence returns its blocks to the pool [F55 §块表].
+  * When blocks run out, the latest arrival is preempted first, and a
+    sequence keeps all of its blocks or gives all of them up; given-up blocks
+    may be moved to host memory and moved back when the sequence resumes
+    [F55 §放不下的时候].  Here: swap_out releases every block of the sequence
+    (their contents are to be copied out first) and keeps its length;
+    swap_in takes fresh blocks for the whole length, all or none.
   * Two sequences may point at the same physical blocks (a fork of one prompt,
     or a shared prefix) [F55 §后来的做法]; [IPX §同一提示生成两个回答的假想例子].
     Blocks carry a reference count.  Before a write into a partially filled
@@ -49,7 +55,8 @@ class OracleAllocator:
         self.refcount = [0] * num_blocks
         self.tables = {}   # seq -> list of physical ids
         self.ctx = {}      # seq -> tokens held
-        self.arrival = []  # sequences in first-come order
+        self.arrival = []  # sequences in first-come order (swapped-out ones keep their place)
+        self.swapped = {}  # seq -> tokens of a sequence preempted by swapping
 
     # -- helpers
     def _take(self):
@@ -68,7 +75,7 @@ class OracleAllocator:
     # -- operations
     def allocate(self, seq, num_tokens):
         """A new sequence whose prompt holds num_tokens: ceil(n / bs) blocks, all or none."""
-        if seq in self.tables:
+        if seq in self.tables or seq in self.swapped:
             raise ValueError("sequence exists")
         if num_tokens < 0:
             raise ValueError("negative length")
@@ -83,7 +90,7 @@ class OracleAllocator:
         """The child's table points at every block of the parent's."""
         if parent not in self.tables:
             raise UnknownSeq()
-        if child in self.tables:
+        if child in self.tables or child in self.swapped:
             raise ValueError("sequence exists")
         self.tables[child] = list(self.tables[parent])
         self.ctx[child] = self.ctx[parent]
@@ -115,12 +122,40 @@ class OracleAllocator:
         return (-1, -1)
 
     def free_seq(self, seq):
+        if seq in self.swapped:
+            del self.swapped[seq]
+            self.arrival.remove(seq)
+            return
         if seq not in self.tables:
             raise UnknownSeq()
         for b in self.tables.pop(seq):
             self._release(b)
         del self.ctx[seq]
         self.arrival.remove(seq)
+
+    def swap_out(self, seq):
+        """Preempt by swapping: the sequence gives up every block (released
+        like a free; the caller copies their contents to host memory first)
+        and keeps its length.  Returns its blocks in logical order."""
+        if seq not in self.tables:
+            raise UnknownSeq()
+        blocks = self.tables.pop(seq)
+        for b in blocks:
+            self._release(b)
+        self.swapped[seq] = self.ctx.pop(seq)
+        return blocks
+
+    def swap_in(self, seq):
+        """Resume a swapped-out sequence: fresh blocks for its whole length,
+        all or none.  Returns them in logical order (the copy-back targets)."""
+        if seq not in self.swapped:
+            raise UnknownSeq()
+        need = -(-self.swapped[seq] // self.block_size)
+        if need > len(self.free):
+            raise OutOfBlocks()
+        self.tables[seq] = [self._take() for _ in range(need)]
+        self.ctx[seq] = self.swapped.pop(seq)
+        return list(self.tables[seq])
 
     def table(self, seq):
         return list(self.tables[seq])
@@ -139,8 +174,12 @@ class OracleAllocator:
         return t, c
 
     def latest_arrival(self):
-        """The sequence preempted first when blocks run out: the latest to arrive."""
-        return self.arrival[-1] if self.arrival else None
+        """The sequence preempted first when blocks run out: the latest to
+        arrive among those holding blocks."""
+        for s in reversed(self.arrival):
+            if s in self.tables:
+                return s
+        return None
 
     def utilisation(self):
         """Tokens held / (blocks in use * block_size), each shared block counted once."""

@@ -13,12 +13,13 @@ LIB_PATH = os.path.join(PKG, "libpagedattn.so")
 PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_OUT_OF_BLOCKS, PA_ERR_UNKNOWN_SEQ = 0, 1, 2, 3
 PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 4, 5, 6
 PA_F32, PA_F16, PA_FP8_E4M3 = 0, 1, 2
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 
 # every symbol the public header declares
 EXPORTS = (
-    "pa_kv_append", "pa_kv_write_prompt", "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode", "pa_decode_step",
-    "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free", "pa_seq_allocate", "pa_seq_fork",
-    "pa_seq_append_slot", "pa_seq_free", "pa_seq_get", "pa_export_tables", "pa_block_refcount",
+    "pa_kv_append", "pa_kv_write_prompt", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode",
+    "pa_decode_step", "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free", "pa_seq_allocate",
+    "pa_seq_fork", "pa_seq_append_slot", "pa_seq_free", "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_get", "pa_export_tables", "pa_block_refcount",
     "pa_allocator_get_stats", "pa_latest_arrival", "pa_status_str", "pa_last_error", "pa_timing_enable",
     "pa_timing_read",
 )
@@ -64,6 +65,7 @@ def lib():
         "pa_kv_append": (st, [P(PaKVCache), vp, vp, i32, vp, vp, i32, i32, vp]),
         "pa_kv_write_prompt": (st, [P(PaKVCache), vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, vp]),
         "pa_copy_blocks": (st, [P(PaKVCache), vp, i32, vp]),
+        "pa_swap_blocks": (st, [P(PaKVCache), vp, vp, vp, i32, i32, vp]),
         "pa_decode_workspace_size": (ctypes.c_size_t, [i32, i32, i32, i32]),
         "pa_decode": (st, [P(PaKVCache), vp, vp, i32, i32, vp, vp, i32, i32, i32, f32, vp, ctypes.c_size_t, vp]),
         "pa_decode_step": (st, [P(PaKVCache), vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, f32, vp,
@@ -75,6 +77,8 @@ def lib():
         "pa_seq_fork": (st, [vp, i32, i32]),
         "pa_seq_append_slot": (st, [vp, i32, P(i32), P(i32)]),
         "pa_seq_free": (st, [vp, i32]),
+        "pa_seq_swap_out": (st, [vp, i32, vp, i32, P(i32)]),
+        "pa_seq_swap_in": (st, [vp, i32, vp, i32, P(i32)]),
         "pa_seq_get": (st, [vp, i32, vp, i32, P(i32), P(i32)]),
         "pa_export_tables": (st, [vp, vp, i32, i32, vp, vp]),
         "pa_block_refcount": (i32, [vp, i32]),

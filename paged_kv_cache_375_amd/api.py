@@ -107,6 +107,27 @@ def copy_blocks(cache: KVCache, src_dst_pairs, stream=None):
                                _stream(stream)))
 
 
+def swap_blocks(cache: KVCache, host_k, host_v, block_ids, direction, stream=None):
+    """Move whole blocks between the pool and pinned host memory (pa_swap_blocks).
+
+    host_k/host_v: pinned CPU tensors [n][num_kv_heads][block_size][head_dim]
+    of the pool dtype (entry i is block block_ids[i]); block_ids: device int32 [n];
+    direction "out" (pool -> host) or "in" (host -> pool)."""
+    _dev(block_ids, torch.int32, "block_ids")
+    if block_ids.dim() != 1:
+        raise ValueError("block_ids must be [n]")
+    n = block_ids.shape[0]
+    shape = (n, cache.num_kv_heads, cache.block_size, cache.head_dim)
+    for name, h in (("host_k", host_k), ("host_v", host_v)):
+        if h.device.type != "cpu" or not h.is_pinned() or not h.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous pinned CPU tensor")
+        if tuple(h.shape) != shape or h.dtype != cache.k.dtype:
+            raise ValueError(f"{name} must be {shape} of {cache.k.dtype}")
+    direction = {"out": _lib.PA_SWAP_OUT, "in": _lib.PA_SWAP_IN}[direction]
+    check(lib().pa_swap_blocks(ctypes.byref(cache.struct), _ptr(host_k), _ptr(host_v), _ptr(block_ids), n, direction,
+                               _stream(stream)))
+
+
 def decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len):
     return int(lib().pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len))
 
@@ -219,6 +240,24 @@ class Allocator:
 
     def free_seq(self, seq):
         self._call(lib().pa_seq_free(self._h, seq))
+
+    def _swap(self, fn, seq):
+        n = ctypes.c_int32()
+        status = fn(self._h, seq, None, 0, ctypes.byref(n))
+        if status == _lib.PA_ERR_INVALID_ARGUMENT and n.value > 0:  # sized: call again with room
+            buf = np.zeros(n.value, dtype=np.int32)
+            self._call(fn(self._h, seq, buf.ctypes.data_as(ctypes.c_void_p), n.value, ctypes.byref(n)))
+            return buf.tolist()
+        self._call(status)
+        return []
+
+    def swap_out(self, seq):
+        """Release every block of seq, keep its length; its former blocks in logical order."""
+        return self._swap(lib().pa_seq_swap_out, seq)
+
+    def swap_in(self, seq):
+        """Fresh blocks for a swapped-out seq's whole length, all or none; in logical order."""
+        return self._swap(lib().pa_seq_swap_in, seq)
 
     def table(self, seq):
         n, c = ctypes.c_int32(), ctypes.c_int32()

@@ -8,7 +8,11 @@
 //   * finished sequences return their blocks;
 //   * forks share blocks with reference counts; a write into a partially
 //     filled block another sequence still references copies it first, the
-//     original's count drops by one, full shared blocks stay shared.
+//     original's count drops by one, full shared blocks stay shared;
+//   * when blocks run out the latest arrival gives all of its blocks up, and
+//     they may be moved to host memory and back: swap-out releases every
+//     block of the sequence and keeps its length, swap-in takes fresh blocks
+//     for the whole length, all or none.
 // The free list is first in, first out; blocks freed together join its tail
 // in logical order.  Every operation validates before it mutates, so a
 // failing call leaves the state unchanged.
@@ -30,7 +34,14 @@ struct pa_allocator {
   std::deque<int32_t> free_list;
   std::vector<int32_t> refcount;
   std::unordered_map<int32_t, Seq> seqs;
-  std::vector<int32_t> arrival;  // first-come order of the live sequences
+  std::unordered_map<int32_t, int32_t> swapped;  // swapped-out sequence -> its context length
+  std::vector<int32_t> arrival;  // first-come order (swapped-out sequences keep their place)
+
+  bool exists(int32_t seq) const { return seqs.count(seq) || swapped.count(seq); }
+  void release(int32_t b) {
+    refcount[b] -= 1;
+    if (refcount[b] == 0) free_list.push_back(b);
+  }
 
   int32_t take() {
     int32_t b = free_list.front();
@@ -82,7 +93,7 @@ extern "C" int32_t pa_allocator_num_free(const pa_allocator* a) {
 extern "C" pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens) {
   if (!a || seq < 0 || num_tokens < 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_allocate: bad argument (seq %d, tokens %d)", seq, num_tokens);
-  if (a->seqs.count(seq)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_allocate: sequence %d exists", seq);
+  if (a->exists(seq)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_allocate: sequence %d exists", seq);
   int64_t need = (static_cast<int64_t>(num_tokens) + a->block_size - 1) / a->block_size;
   if (need > static_cast<int64_t>(a->free_list.size()))
     return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_allocate: sequence %d needs %lld blocks, %zu free", seq,
@@ -100,7 +111,7 @@ extern "C" pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child)
   if (!a || child < 0) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_fork: bad argument");
   auto it = a->seqs.find(parent);
   if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_fork: unknown parent %d", parent);
-  if (a->seqs.count(child)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_fork: sequence %d exists", child);
+  if (a->exists(child)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_fork: sequence %d exists", child);
   pa_allocator::Seq s = it->second;
   for (int32_t b : s.blocks) a->refcount[b] += 1;
   a->seqs.emplace(child, std::move(s));
@@ -140,14 +151,58 @@ extern "C" pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* c
 
 extern "C" pa_status pa_seq_free(pa_allocator* a, int32_t seq) {
   if (!a) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_free: NULL allocator");
+  auto sw = a->swapped.find(seq);
+  if (sw != a->swapped.end()) {
+    a->swapped.erase(sw);
+    a->arrival.erase(std::find(a->arrival.begin(), a->arrival.end(), seq));
+    return ok();
+  }
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_free: unknown sequence %d", seq);
-  for (int32_t b : it->second.blocks) {
-    a->refcount[b] -= 1;
-    if (a->refcount[b] == 0) a->free_list.push_back(b);
-  }
+  for (int32_t b : it->second.blocks) a->release(b);
   a->seqs.erase(it);
   a->arrival.erase(std::find(a->arrival.begin(), a->arrival.end(), seq));
+  return ok();
+}
+
+extern "C" pa_status pa_seq_swap_out(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
+                                     int32_t* num_blocks) {
+  if (!a || !num_blocks || cap < 0 || (cap > 0 && !block_ids))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_swap_out: bad argument");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_swap_out: no resident sequence %d", seq);
+  const auto& blocks = it->second.blocks;
+  *num_blocks = static_cast<int32_t>(blocks.size());
+  if (static_cast<int64_t>(blocks.size()) > cap)
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_swap_out: %zu blocks, room for %d", blocks.size(), cap);
+  for (size_t j = 0; j < blocks.size(); ++j) block_ids[j] = blocks[j];
+  for (int32_t b : blocks) a->release(b);
+  a->swapped.emplace(seq, it->second.ctx);
+  a->seqs.erase(it);
+  return ok();
+}
+
+extern "C" pa_status pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
+                                    int32_t* num_blocks) {
+  if (!a || !num_blocks || cap < 0 || (cap > 0 && !block_ids))
+    return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_swap_in: bad argument");
+  auto sw = a->swapped.find(seq);
+  if (sw == a->swapped.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_swap_in: no swapped-out sequence %d", seq);
+  const int64_t need = (static_cast<int64_t>(sw->second) + a->block_size - 1) / a->block_size;
+  *num_blocks = static_cast<int32_t>(need);
+  if (need > cap) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_swap_in: %lld blocks, room for %d",
+                              static_cast<long long>(need), cap);
+  if (need > static_cast<int64_t>(a->free_list.size()))
+    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_swap_in: sequence %d needs %lld blocks, %zu free", seq,
+                static_cast<long long>(need), a->free_list.size());
+  pa_allocator::Seq s;
+  s.ctx = sw->second;
+  for (int64_t i = 0; i < need; ++i) {
+    s.blocks.push_back(a->take());
+    block_ids[i] = s.blocks.back();
+  }
+  a->seqs.emplace(seq, std::move(s));
+  a->swapped.erase(sw);
   return ok();
 }
 
@@ -215,6 +270,8 @@ extern "C" pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_
 }
 
 extern "C" int32_t pa_latest_arrival(const pa_allocator* a) {
-  if (!a || a->arrival.empty()) return -1;
-  return a->arrival.back();
+  if (!a) return -1;
+  for (auto it = a->arrival.rbegin(); it != a->arrival.rend(); ++it)
+    if (a->seqs.count(*it)) return *it;
+  return -1;
 }

@@ -111,6 +111,28 @@ extern "C" pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src
   return hip_status(pa::launch_copy_blocks(*cache, src_dst_pairs, n, static_cast<hipStream_t>(stream)), fn);
 }
 
+extern "C" pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, const int32_t* block_ids,
+                                    int32_t n, int32_t direction, void* stream) {
+  static const char* fn = "pa_swap_blocks";
+  if (pa_status s = check_cache(cache, fn)) return s;
+  if (n < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: negative block count", fn);
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: direction %d", fn, direction);
+  if (n == 0) return ok();
+  if (!host_k || !host_v || !block_ids) return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL pointer", fn);
+  // The kernel reaches host memory through its device mapping; memory the
+  // runtime does not know as pinned is refused here rather than faulting.
+  void* dk = nullptr;
+  void* dv = nullptr;
+  if (hipHostGetDevicePointer(&dk, host_k, 0) != hipSuccess || hipHostGetDevicePointer(&dv, host_v, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: host buffers must be pinned host memory (hipHostMalloc)", fn);
+  }
+  return hip_status(pa::launch_swap_blocks(*cache, dk, dv, block_ids, n, direction == PA_SWAP_OUT,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 // Workspace: arrival counters [num_seqs][num_q_heads] int32 (padded to 256
 // bytes), then (max, sum) pairs and unnormalised vectors per partition.
 static size_t counters_bytes(int32_t num_seqs, int32_t num_q_heads) {

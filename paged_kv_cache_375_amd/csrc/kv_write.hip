@@ -1,5 +1,6 @@
 // Kernels that write the paged pool: append of the new token, the prompt's
-// bulk write, and the block copy of copy-on-write.
+// bulk write, the block copy of copy-on-write, and the block moves between
+// the pool and host memory of preemption by swapping.
 //
 // Pool layout: [num_blocks][num_kv_heads][block_size][head_dim] for K and V.
 // Each thread moves one 16-byte chunk of the source vector (4 f32 or 8 f16
@@ -107,6 +108,34 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(char* __restrict_
   }
 }
 
+// Block moves between the pool and pinned host memory, one launch for the
+// whole list: entry i of the host buffers is block ids[i].  Each thread moves
+// 16-byte chunks of the flattened (entry, chunk) range, so consecutive lanes
+// touch consecutive host bytes whatever the block size, and the host link
+// sees many requests in flight at once.
+template <bool TO_HOST>
+__global__ __launch_bounds__(kThreads) void swap_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc,
+                                                               char* __restrict__ hk, char* __restrict__ hv,
+                                                               const int32_t* __restrict__ ids, int64_t n,
+                                                               int num_blocks, int64_t chunks) {
+  const int64_t total = n * chunks;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; idx < total; idx += stride) {
+    const int64_t i = idx / chunks;
+    const int blk = ids[i];
+    if (blk < 0 || blk >= num_blocks) continue;
+    const int64_t pool = (static_cast<int64_t>(blk) * chunks + (idx - i * chunks)) * 16;
+    const int64_t host = idx * 16;
+    if (TO_HOST) {
+      store16(hk + host, load16(kc + pool));
+      store16(hv + host, load16(vc + pool));
+    } else {
+      store16(kc + pool, load16(hk + host));
+      store16(vc + pool, load16(hv + host));
+    }
+  }
+}
+
 template <typename ACT, typename KV>
 hipError_t append_t(const pa_kv_cache& c, const void* k_new, const void* v_new, const int32_t* tables,
                     const int32_t* ctx, int num_seqs, int max_blocks, hipStream_t st) {
@@ -181,6 +210,20 @@ hipError_t launch_copy_blocks(const pa_kv_cache& c, const int32_t* pairs, int n,
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<unsigned>(gx), n), dim3(kThreads), 0, st,
                      static_cast<char*>(c.k_cache), static_cast<char*>(c.v_cache), pairs, c.num_blocks,
                      block_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(const pa_kv_cache& c, void* host_k, void* host_v, const int32_t* ids, int n,
+                              bool to_host, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int64_t elem = c.kv_dtype == PA_F32 ? 4 : c.kv_dtype == PA_F16 ? 2 : 1;
+  const int64_t chunks = static_cast<int64_t>(c.num_kv_heads) * c.block_size * c.head_dim * elem / 16;
+  int64_t gx = (static_cast<int64_t>(n) * chunks + kThreads - 1) / kThreads;
+  if (gx > 4096) gx = 4096;
+  auto kern = to_host ? swap_blocks_kernel<true> : swap_blocks_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(gx)), dim3(kThreads), 0, st, static_cast<char*>(c.k_cache),
+                     static_cast<char*>(c.v_cache), static_cast<char*>(host_k), static_cast<char*>(host_v), ids,
+                     static_cast<int64_t>(n), c.num_blocks, chunks);
   return hipGetLastError();
 }
 

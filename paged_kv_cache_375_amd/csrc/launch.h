@@ -24,6 +24,8 @@ hipError_t launch_write_prompt(const pa_kv_cache& c, const void* k_src, const vo
                                const int64_t* src_row, const int32_t* start_pos, const int32_t* count,
                                const int32_t* tables, int num_seqs, int max_blocks, int max_count, hipStream_t st);
 hipError_t launch_copy_blocks(const pa_kv_cache& c, const int32_t* pairs, int n, hipStream_t st);
+hipError_t launch_swap_blocks(const pa_kv_cache& c, void* host_k, void* host_v, const int32_t* ids, int n,
+                              bool to_host, hipStream_t st);
 
 struct DecodeArgs {
   const pa_kv_cache* cache;

@@ -86,19 +86,50 @@ def test_append_and_copy_argument_checks():
     assert L.pa_copy_blocks(ctypes.byref(c), None, 0, None) == _lib.PA_OK
     assert L.pa_kv_write_prompt(ctypes.byref(c), 0x1, 0x1, _lib.PA_F16, 0x1, 0x1, 0x1, 0x1, 70000, 4, 4,
                                 None) == _lib.PA_ERR_UNSUPPORTED
+    assert L.pa_swap_blocks(ctypes.byref(c), 0x1, 0x1, None, 3, _lib.PA_SWAP_OUT, None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_swap_blocks(ctypes.byref(c), None, 0x1, 0x1, 3, _lib.PA_SWAP_IN, None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_swap_blocks(ctypes.byref(c), 0x1, 0x1, 0x1, 3, 2, None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_swap_blocks(ctypes.byref(c), 0x1, 0x1, 0x1, -1, _lib.PA_SWAP_IN, None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_swap_blocks(ctypes.byref(c), None, None, None, 0, _lib.PA_SWAP_OUT, None) == _lib.PA_OK
 
 
+def test_swap_calls_size_first_and_change_nothing_on_failure():
+    a = Allocator(6, 4, [5, 4, 3, 2, 1, 0])
+    a.allocate(0, 9)  # three blocks
+    n = ctypes.c_int32(-1)
+    L = _lib.lib()
+    assert L.pa_seq_swap_out(a._h, 0, None, 0, ctypes.byref(n)) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert n.value == 3 and a.num_free() == 3 and a.table(0) == [5, 4, 3]
+    assert L.pa_seq_swap_out(a._h, 7, None, 0, ctypes.byref(n)) == _lib.PA_ERR_UNKNOWN_SEQ
+    assert a.swap_out(0) == [5, 4, 3] and a.num_free() == 6 and a.latest_arrival() is None
+    a.allocate(1, 16)  # four blocks: two left
+    with pytest.raises(OutOfBlocks):
+        a.swap_in(0)
+    assert a.num_free() == 2
+    with pytest.raises(_lib.PagedAttnError):
+        a.append_slot(0)  # not resident
+    a.free_seq(1)
+    assert a.swap_in(0) == [4, 3, 2] and a.table(0) == [4, 3, 2] and a.latest_arrival() == 0  # FIFO free list
+
+
+@pytest.mark.parametrize("swaps", [False, True], ids=["no_swap", "swap"])
 @pytest.mark.parametrize("bs", [1, 4, 16])
 @pytest.mark.parametrize("seed", [0, 1])
-def test_cpp_allocator_matches_reference_exactly(bs, seed):
+def test_cpp_allocator_matches_reference_exactly(bs, seed, swaps):
     rng = np.random.default_rng(seed)
     nb = 32
     order = rng.permutation(nb)
     ref, lib_a = OracleAllocator(nb, bs, order), Allocator(nb, bs, order)
-    live, nxt = [], 0
+    live, out, nxt = [], [], 0
     for _ in range(500):
-        op = int(rng.integers(0, 10))
-        if op < 2 or not live:
+        op = int(rng.integers(0, 13 if swaps else 10))
+        if op == 10 and live:
+            name, args, new = "swap_out", (int(rng.choice(live)),), None
+        elif op >= 11 and out:
+            name, args, new = "swap_in", (int(rng.choice(out)),), None
+        elif op == 9 and out and rng.integers(0, 2):
+            name, args, new = "free_seq", (int(rng.choice(out)),), None
+        elif op < 2 or not live or op >= 10:
             name, args, new = "allocate", (nxt, int(rng.integers(0, 3 * bs + 1))), nxt
         elif op < 3:
             name, args, new = "fork", (int(rng.choice(live)), nxt), nxt
@@ -122,7 +153,11 @@ def test_cpp_allocator_matches_reference_exactly(bs, seed):
                 live.append(new)
                 nxt += 1
             if name == "free_seq":
-                live.remove(args[0])
+                (out if args[0] in out else live).remove(args[0])
+            if name == "swap_out":
+                live.remove(args[0]); out.append(args[0])
+            if name == "swap_in":
+                out.remove(args[0]); live.append(args[0])
         assert ref.num_free() == lib_a.num_free()
         for s in ref.tables:
             assert ref.table(s) == lib_a.table(s)

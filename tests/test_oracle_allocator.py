@@ -23,16 +23,39 @@ def check_invariants(a: OracleAllocator):
 
 
 def snapshot(a):
-    return (list(a.free), list(a.refcount), {s: list(t) for s, t in a.tables.items()}, dict(a.ctx), list(a.arrival))
+    return (list(a.free), list(a.refcount), {s: list(t) for s, t in a.tables.items()}, dict(a.ctx), list(a.arrival),
+            dict(a.swapped))
 
 
-def random_trace(a, rng, steps, max_seq=12):
-    live = []
+def random_trace(a, rng, steps, max_seq=12, swaps=False):
+    live, out = [], []
     nxt = 0
     for _ in range(steps):
-        op = rng.integers(0, 10)
+        op = rng.integers(0, 13 if swaps else 10)
         before = snapshot(a)
         try:
+            if op == 10 and live:
+                s = int(rng.choice(live))
+                rc_before, held = list(a.refcount), list(a.tables[s])
+                assert a.swap_out(s) == held
+                live.remove(s); out.append(s)
+                # every block drops one reference; the length is kept
+                assert all(a.refcount[b] == rc_before[b] - held.count(b) for b in set(held))
+                assert a.swapped[s] == before[3][s] and s not in a.tables
+                check_invariants(a)
+                continue
+            if op >= 11 and out:
+                s = int(rng.choice(out))
+                got = a.swap_in(s)
+                out.remove(s); live.append(s)
+                # fresh, unshared blocks that exactly cover the kept length
+                assert len(got) == -(-a.ctx[s] // a.block_size) and a.ctx[s] == before[5][s]
+                assert all(a.refcount[b] == 1 for b in got) and len(set(got)) == len(got)
+                assert all(b in before[0] for b in got)
+                check_invariants(a)
+                continue
+            if op >= 10:
+                continue
             if op < 2 or not live:
                 a.allocate(nxt, int(rng.integers(0, 3 * a.block_size + 1)))
                 live.append(nxt); nxt += 1
@@ -51,6 +74,11 @@ def random_trace(a, rng, steps, max_seq=12):
                 if src >= 0:
                     assert rc_before[src] > 1 and a.refcount[src] == rc_before[src] - 1
                     assert table_before[last] == src and target == dst
+            elif out and rng.integers(0, 2):
+                s = int(rng.choice(out))
+                a.free_seq(s)  # a swapped-out sequence may finish without resuming
+                out.remove(s)
+                assert s not in a.swapped and s not in a.arrival
             else:
                 s = int(rng.choice(live))
                 a.free_seq(s)
@@ -58,9 +86,12 @@ def random_trace(a, rng, steps, max_seq=12):
         except OutOfBlocks:
             assert snapshot(a) == before  # a failed call changes nothing
         check_invariants(a)
+        assert a.latest_arrival() == next((q for q in reversed(a.arrival) if q in a.tables), None)
         if len(live) > max_seq:
             s = live.pop(0)
             a.free_seq(s)
+    for s in out:
+        a.free_seq(s)
     return live
 
 
@@ -75,6 +106,50 @@ def test_random_traces_keep_invariants(bs, seed):
         a.free_seq(s)
     # freeing every sequence restores every block
     assert sorted(a.free) == list(range(nb)) and all(c == 0 for c in a.refcount)
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+@pytest.mark.parametrize("seed", [3, 4])
+def test_random_traces_with_swapping_keep_invariants(bs, seed):
+    rng = np.random.default_rng(seed)
+    nb = 24
+    a = OracleAllocator(nb, bs, rng.permutation(nb))
+    live = random_trace(a, rng, 600, swaps=True)
+    for s in list(live):
+        a.free_seq(s)
+    assert sorted(a.free) == list(range(nb)) and all(c == 0 for c in a.refcount)
+    assert not a.swapped and not a.arrival
+
+
+def test_preemption_by_swapping_latest_arrival_first():
+    """Blocks run out: the latest arrival gives up all of its blocks, the
+    earlier one proceeds, and the preempted one resumes whole once blocks
+    are back [F55 §放不下的时候]."""
+    a = OracleAllocator(4, 2, [0, 1, 2, 3])
+    a.allocate(0, 3)                   # blocks [0, 1]
+    a.allocate(1, 4)                   # blocks [2, 3]
+    a.append_slot(0)                   # ctx 4: still two blocks
+    with pytest.raises(OutOfBlocks):
+        a.append_slot(0)               # ctx 5 needs a third block
+    victim = a.latest_arrival()
+    assert victim == 1
+    assert a.swap_out(1) == [2, 3] and a.num_free() == 2
+    assert a.latest_arrival() == 0     # a swapped-out sequence is not preempted again
+    assert a.append_slot(0) == (-1, -1) and a.table(0) == [0, 1, 2]
+    with pytest.raises(OutOfBlocks):
+        a.swap_in(1)                   # needs 2 blocks, 1 free: all or none
+    assert a.swapped == {1: 4} and a.num_free() == 1
+    with pytest.raises(ValueError):
+        a.allocate(1, 1)               # the id is still taken
+    a.free_seq(0)
+    assert a.swap_in(1) == [3, 0] and a.ctx[1] == 4 and a.latest_arrival() == 1
+    with pytest.raises(UnknownSeq):
+        a.swap_in(1)
+    # a fork's shared blocks stay with the other holder
+    a.fork(1, 2)
+    assert a.swap_out(2) == [3, 0] and a.refcount[3] == 1 and a.refcount[0] == 1
+    a.free_seq(2)
+    assert 2 not in a.arrival
 
 
 def test_fifo_order_and_all_or_nothing():
