@@ -296,6 +296,42 @@ pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out)
  * among those holding blocks [F55 §放不下的时候]; -1 if none. */
 int32_t pa_latest_arrival(const pa_allocator* a);
 
+/*
+ * The toy machine's arrival simulator [F55 §实验台], run over this
+ * allocator.  Sequence i arrives at round arrivals[i] and writes one token
+ * per round until it has lengths[i] tokens, then leaves.  Each round:
+ *   1. Growth: running sequences take this round's slot, earliest arrival
+ *      first.  When no block is free, the latest arrival (pa_latest_arrival)
+ *      is preempted by swapping [F55 §放不下的时候]: it keeps its tokens
+ *      and rejoins the queue; if it is the sequence asking, that one writes
+ *      nothing this round.
+ *   2. Admission, only in a round without preemption: queued sequences
+ *      strictly first come, first served (arrival round, then index) while
+ *      the head's whole need, ceil((tokens + 1) / block_size) blocks, is
+ *      free; the rest wait.
+ *   3. Readout: running sequences, tokens held, and slots reserved (blocks
+ *      in use x block_size).
+ *   4. Departure of finished sequences.
+ * The page's row option (each sequence reserves the maximum length on
+ * arrival) is block_size = max length with floor(slots / max length) blocks.
+ * Readouts: the most sequences running in one round; utilisation, the mean
+ * over rounds that reserve anything of held / reserved; the rounds until
+ * all have left; preemptions.  trace (host, NULL allowed) receives up to
+ * trace_cap rounds of (running, held, reserved) int32 triples.
+ * PA_ERR_INVALID_ARGUMENT for lengths < 1, arrivals < 0, or a sequence
+ * longer than the whole pool.  Host only; allocates its own allocator.
+ */
+typedef struct {
+  int32_t max_concurrent;
+  int32_t rounds;
+  int32_t preemptions;
+  int32_t reserved0;
+  double utilisation;
+} pa_arrival_readout;
+pa_status pa_simulate_arrivals(int32_t num_blocks, int32_t block_size, const int32_t* arrivals,
+                               const int32_t* lengths, int32_t n, pa_arrival_readout* out, int32_t* trace,
+                               int32_t trace_cap);
+
 /* ================================ utilities ================================ */
 
 const char* pa_status_str(pa_status s);

@@ -20,7 +20,7 @@ EXPORTS = (
     "pa_kv_append", "pa_kv_write_prompt", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_step", "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free", "pa_seq_allocate",
     "pa_seq_fork", "pa_seq_append_slot", "pa_seq_free", "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_get", "pa_export_tables", "pa_block_refcount",
-    "pa_allocator_get_stats", "pa_latest_arrival", "pa_status_str", "pa_last_error", "pa_timing_enable",
+    "pa_allocator_get_stats", "pa_latest_arrival", "pa_simulate_arrivals", "pa_status_str", "pa_last_error", "pa_timing_enable",
     "pa_timing_read",
 )
 
@@ -39,6 +39,13 @@ class PaAllocatorStats(ctypes.Structure):
     _fields_ = [
         ("num_blocks", ctypes.c_int32), ("num_free", ctypes.c_int32), ("num_shared", ctypes.c_int32),
         ("num_seqs", ctypes.c_int32), ("tokens_held", ctypes.c_int64), ("slots_allocated", ctypes.c_int64),
+    ]
+
+
+class PaArrivalReadout(ctypes.Structure):
+    _fields_ = [
+        ("max_concurrent", ctypes.c_int32), ("rounds", ctypes.c_int32), ("preemptions", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32), ("utilisation", ctypes.c_double),
     ]
 
 
@@ -84,6 +91,7 @@ def lib():
         "pa_block_refcount": (i32, [vp, i32]),
         "pa_allocator_get_stats": (st, [vp, P(PaAllocatorStats)]),
         "pa_latest_arrival": (i32, [vp]),
+        "pa_simulate_arrivals": (st, [i32, i32, vp, vp, i32, P(PaArrivalReadout), vp, i32]),
         "pa_status_str": (ctypes.c_char_p, [st]),
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_timing_enable": (st, [i32]),

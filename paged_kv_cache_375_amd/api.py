@@ -286,3 +286,22 @@ class Allocator:
     def latest_arrival(self):
         r = lib().pa_latest_arrival(self._h)
         return None if r < 0 else r
+
+
+def simulate_arrivals(num_blocks, block_size, arrivals, lengths, trace_rounds=0):
+    """The toy machine's arrival simulator (pa_simulate_arrivals), run over the library's allocator.
+
+    Returns dict(max_concurrent, utilisation, rounds, preemptions, trace), trace holding
+    (running, tokens held, slots reserved) for the first trace_rounds rounds."""
+    arr = np.ascontiguousarray(arrivals, dtype=np.int32)
+    lens = np.ascontiguousarray(lengths, dtype=np.int32)
+    if arr.shape != lens.shape or arr.ndim != 1:
+        raise ValueError("arrivals and lengths must be 1-D of equal length")
+    out = _lib.PaArrivalReadout()
+    tr = np.zeros((max(1, trace_rounds), 3), dtype=np.int32)
+    check(lib().pa_simulate_arrivals(num_blocks, block_size, arr.ctypes.data_as(ctypes.c_void_p),
+                                     lens.ctypes.data_as(ctypes.c_void_p), len(arr), ctypes.byref(out),
+                                     tr.ctypes.data_as(ctypes.c_void_p), trace_rounds))
+    return {"max_concurrent": out.max_concurrent, "utilisation": out.utilisation, "rounds": out.rounds,
+            "preemptions": out.preemptions,
+            "trace": [tuple(int(x) for x in row) for row in tr[: min(trace_rounds, out.rounds)]]}
