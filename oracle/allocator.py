@@ -24,6 +24,18 @@ The rules, in the pages' words restated:
     blocks stay shared; blocks nobody references are reclaimed
     [F55 §常见问题 (copy-on-write)]; [IPX §同一提示生成两个回答的假想例子].
 
+  * Automatic prefix caching: every full block is keyed by its tokens and
+    all the content before it; a new sequence whose beginning matches reuses
+    the existing blocks, which saves prompt processing, not generation
+    [F55 §后来的做法].  The same tokens at another position are other
+    content and are not shared [F55 §模型省略了什么].  Here the key is the
+    whole token prefix up to the block's end, compared exactly (no hash).
+    Reuse stops at the first block that misses; only full prompt blocks are
+    keyed; a block keeps its key after its last holder frees it and loses it
+    when it is taken for other content (first in, first out, so the least
+    recently freed block goes first); a key already held by another block is
+    not taken over.
+
 Readings where the pages are silent:
   * free list order: first in, first out (allocation pops the head, a freed
     block joins the tail); blocks freed together join in logical order.
@@ -57,11 +69,15 @@ class OracleAllocator:
         self.ctx = {}      # seq -> tokens held
         self.arrival = []  # sequences in first-come order (swapped-out ones keep their place)
         self.swapped = {}  # seq -> tokens of a sequence preempted by swapping
+        self.cache = {}    # full token prefix (tuple) -> block holding its last bs tokens
+        self.key = {}      # block -> its prefix key, while it keeps one
 
     # -- helpers
     def _take(self):
         b = self.free.popleft()
         self.refcount[b] = 1
+        if b in self.key:  # taken for other content: its cached prefix is gone
+            del self.cache[self.key.pop(b)]
         return b
 
     def _release(self, b):
@@ -85,6 +101,42 @@ class OracleAllocator:
         self.tables[seq] = [self._take() for _ in range(need)]
         self.ctx[seq] = num_tokens
         self.arrival.append(seq)
+
+    def allocate_cached(self, seq, tokens):
+        """A new sequence with prompt `tokens`, reusing cached full blocks
+        whose whole prefix matches.  All or none.  Returns the number of
+        leading tokens whose K/V are already in the reused blocks."""
+        if seq in self.tables or seq in self.swapped:
+            raise ValueError("sequence exists")
+        tokens = tuple(int(t) for t in tokens)
+        bs, n = self.block_size, len(tokens)
+        need = -(-n // bs)
+        hits = []
+        while len(hits) < n // bs:
+            b = self.cache.get(tokens[: (len(hits) + 1) * bs])
+            if b is None:
+                break
+            hits.append(b)
+        claimed = sum(1 for b in hits if self.refcount[b] == 0)
+        if need - len(hits) + claimed > len(self.free):
+            raise OutOfBlocks()
+        table = []
+        for b in hits:
+            if self.refcount[b] == 0:
+                self.free.remove(b)
+            self.refcount[b] += 1
+            table.append(b)
+        for j in range(len(hits), need):
+            b = self._take()
+            table.append(b)
+            k = tokens[: (j + 1) * bs]
+            if (j + 1) * bs <= n and k not in self.cache:
+                self.cache[k] = b
+                self.key[b] = k
+        self.tables[seq] = table
+        self.ctx[seq] = n
+        self.arrival.append(seq)
+        return len(hits) * bs
 
     def fork(self, parent, child):
         """The child's table points at every block of the parent's."""

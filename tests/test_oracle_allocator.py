@@ -185,3 +185,101 @@ def test_fork_shares_full_blocks_and_copies_partial_last_block_once():
     a.fork(0, 2)
     a.allocate(3, 0)
     assert a.table(2)[:2] == [0, 1] and a.refcount[0] == 3
+
+
+def test_prefix_cache_reuses_blocks_of_a_matching_prefix_only():
+    """Full blocks are keyed by their tokens and everything before them
+    [F55 §后来的做法]; the same tokens at another position are other content
+    [F55 §模型省略了什么]."""
+    a = OracleAllocator(16, 4)
+    toks = list(range(10))                                  # 2 full blocks + 2 tokens
+    assert a.allocate_cached(0, toks) == 0 and a.table(0) == [0, 1, 2]
+    assert a.allocate_cached(1, toks) == 8 and a.table(1) == [0, 1, 3]   # the partial block is never shared
+    assert a.refcount[:4] == [2, 2, 1, 1]
+    assert a.allocate_cached(2, toks[:4] + [99] * 6) == 4 and a.table(2) == [0, 4, 5]
+    assert a.allocate_cached(3, [99] * 4 + toks[4:8]) == 0   # block 1's tokens, but another prefix
+    assert a.allocate_cached(4, [0, 1, 2, 3] * 2) == 4       # the repeat sits at another position
+    check_invariants(a)
+
+
+def test_prefix_cache_survives_free_until_blocks_are_taken_again():
+    a = OracleAllocator(6, 2, [0, 1, 2, 3, 4, 5])
+    a.allocate_cached(0, [7, 8, 9, 10, 11])                  # blocks 0, 1 keyed; 2 partial
+    a.free_seq(0)
+    assert list(a.free) == [3, 4, 5, 0, 1, 2]
+    assert a.allocate_cached(1, [7, 8, 9, 10]) == 4 and a.table(1) == [0, 1]  # claimed back from the free list
+    assert list(a.free) == [3, 4, 5, 2]
+    a.free_seq(1)
+    a.allocate(2, 8)                                          # takes 3, 4, 5, 2: no key is lost yet
+    # block 0 is claimed back; the partial block is the free list's head, block 1,
+    # whose key (7, 8, 9, 10) is dropped as it is taken for other content
+    assert a.allocate_cached(3, [7, 8, 1]) == 2 and a.table(3) == [0, 1]
+    assert a.cache == {(7, 8): 0}
+    a.free_seq(3)
+    a.free_seq(2)
+    assert list(a.free) == [0, 1, 3, 4, 5, 2]
+    a.allocate(4, 2)                                          # takes block 0: the key (7, 8) goes too
+    assert a.allocate_cached(5, [7, 8, 9, 10]) == 0 and a.table(5) == [1, 3]
+    assert a.cache == {(7, 8): 1, (7, 8, 9, 10): 3}
+    with pytest.raises(OutOfBlocks):
+        a.allocate_cached(6, [7, 8] + [0] * 30)               # all or none
+    assert a.refcount[1] == 1 and 6 not in a.tables
+    check_invariants(a)
+
+
+@pytest.mark.parametrize("bs", [1, 2, 4, 16])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_cache_keeps_every_sequence_reading_its_own_tokens(bs, seed):
+    """A ghost pool holds token ids in place of K/V: prompts write only their
+    uncached tail, appends write a fresh token, copy-on-write copies blocks.
+    Every live sequence must read back exactly its own tokens through its
+    table, whatever it reused."""
+    rng = np.random.default_rng(seed)
+    nb = 40
+    a = OracleAllocator(nb, bs, rng.permutation(nb))
+    content = [[None] * bs for _ in range(nb)]
+    hist = {}
+    systems = [rng.integers(0, 5, 3 * bs + 1).tolist() for _ in range(3)]
+    live, nxt = [], 0
+    for _ in range(500):
+        op = int(rng.integers(0, 10))
+        try:
+            if op < 3 or not live:
+                toks = list(systems[int(rng.integers(0, 3))])[: int(rng.integers(0, 3 * bs + 2))]
+                toks += rng.integers(0, 5, int(rng.integers(0, 2 * bs))).tolist()
+                cached = a.allocate_cached(nxt, toks)
+                assert cached % bs == 0 and toks[:cached] == [
+                    content[a.tables[nxt][p // bs]][p % bs] for p in range(cached)]
+                for p in range(cached, len(toks)):
+                    content[a.tables[nxt][p // bs]][p % bs] = toks[p]
+                hist[nxt] = toks
+                live.append(nxt); nxt += 1
+            elif op < 4:
+                p = int(rng.choice(live))
+                a.fork(p, nxt)
+                hist[nxt] = list(hist[p])
+                live.append(nxt); nxt += 1
+            elif op < 9:
+                s = int(rng.choice(live))
+                src, dst = a.append_slot(s)
+                if src >= 0:
+                    content[dst] = list(content[src])
+                pos = a.ctx[s] - 1
+                t = int(rng.integers(0, 5))
+                content[a.tables[s][pos // bs]][pos % bs] = t
+                hist[s].append(t)
+            else:
+                s = int(rng.choice(live))
+                a.free_seq(s)
+                live.remove(s)
+        except OutOfBlocks:
+            pass
+        check_invariants(a)
+        for k, b in a.cache.items():
+            assert a.key[b] == k and len(k) % bs == 0
+            assert content[b] == list(k[-bs:])                 # a keyed block holds its key's last tokens
+        for s in live:
+            assert [content[a.tables[s][p // bs]][p % bs] for p in range(a.ctx[s])] == hist[s]
+        if len(live) > 10:
+            s = live.pop(0)
+            a.free_seq(s)
