@@ -257,6 +257,30 @@ void pa_allocator_destroy(pa_allocator* a);
 int32_t pa_allocator_num_free(const pa_allocator* a);
 /* A new sequence holding num_tokens (>= 0) tokens: ceil(n / block_size) blocks. */
 pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens);
+/*
+ * Automatic prefix caching [F55 §后来的做法]: allocate a sequence whose
+ * prompt is tokens[0, num_tokens) (host int32 token ids), reusing blocks
+ * that already hold the same beginning.  Every full block is keyed by its
+ * tokens and by everything before it, through a chained 64-bit hash (the
+ * FNV-1a hash of the previous block's key and the block's tokens).  A
+ * lookup also compares the stored tokens and previous key.  The same
+ * tokens at another position are another key.  Reuse stops at the first
+ * full block that misses.  A reused block gains one reference (one that
+ * had been freed is taken back off the free list); the other blocks are
+ * new, and the new full ones become keys unless the key is already held.
+ * A block keeps its key after its last holder frees it, and loses it when
+ * the free list hands it out for other content (least recently freed
+ * first).  *num_cached_tokens receives the number of leading tokens whose
+ * K/V the reused blocks already hold: the caller writes only
+ * [*num_cached_tokens, num_tokens) (pa_kv_write_prompt with that start).
+ * This saves prompt processing; it does not change decode.  All or none:
+ * PA_ERR_OUT_OF_BLOCKS changes nothing.  Blocks filled later by appends
+ * are not keyed.
+ */
+pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const int32_t* tokens, int32_t num_tokens,
+                                 int32_t* num_cached_tokens);
+/* Number of blocks that currently hold a prefix-cache key (-1 if a is NULL). */
+int32_t pa_prefix_cache_size(const pa_allocator* a);
 /* child shares every block of parent (reference counts + 1). */
 pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child);
 /* Reserve the slot of one more token.  *cow_src / *cow_dst receive the block

@@ -19,9 +19,10 @@ PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 EXPORTS = (
     "pa_kv_append", "pa_kv_write_prompt", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_step", "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free", "pa_seq_allocate",
-    "pa_seq_fork", "pa_seq_append_slot", "pa_seq_free", "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_get", "pa_export_tables", "pa_block_refcount",
-    "pa_allocator_get_stats", "pa_latest_arrival", "pa_simulate_arrivals", "pa_status_str", "pa_last_error", "pa_timing_enable",
-    "pa_timing_read",
+    "pa_seq_allocate_cached", "pa_prefix_cache_size", "pa_seq_fork", "pa_seq_append_slot", "pa_seq_free",
+    "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_get", "pa_export_tables", "pa_block_refcount",
+    "pa_allocator_get_stats", "pa_latest_arrival", "pa_simulate_arrivals", "pa_status_str", "pa_last_error",
+    "pa_timing_enable", "pa_timing_read",
 )
 
 
@@ -81,6 +82,8 @@ def lib():
         "pa_allocator_destroy": (None, [vp]),
         "pa_allocator_num_free": (i32, [vp]),
         "pa_seq_allocate": (st, [vp, i32, i32]),
+        "pa_seq_allocate_cached": (st, [vp, i32, vp, i32, P(i32)]),
+        "pa_prefix_cache_size": (i32, [vp]),
         "pa_seq_fork": (st, [vp, i32, i32]),
         "pa_seq_append_slot": (st, [vp, i32, P(i32), P(i32)]),
         "pa_seq_free": (st, [vp, i32]),

@@ -210,13 +210,14 @@ class Allocator:
                                         order.ctypes.data_as(ctypes.c_void_p) if order is not None else None,
                                         ctypes.byref(h)))
         self._h = h
+        self._destroy = lib().pa_allocator_destroy  # kept: the module may be torn down before __del__
         self._order = order
         self.num_blocks, self.block_size = num_blocks, block_size
 
     def __del__(self):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            lib().pa_allocator_destroy(h)
+            self._destroy(h)
             self._h = None
 
     def _call(self, status):
@@ -229,6 +230,18 @@ class Allocator:
 
     def allocate(self, seq, num_tokens):
         self._call(lib().pa_seq_allocate(self._h, seq, num_tokens))
+
+    def allocate_cached(self, seq, tokens):
+        """A new sequence with prompt token ids `tokens`, reusing cached full blocks of the same
+        beginning; returns how many leading tokens the reused blocks already hold."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        cached = ctypes.c_int32()
+        self._call(lib().pa_seq_allocate_cached(self._h, seq, toks.ctypes.data_as(ctypes.c_void_p), len(toks),
+                                                ctypes.byref(cached)))
+        return cached.value
+
+    def prefix_cache_size(self):
+        return lib().pa_prefix_cache_size(self._h)
 
     def fork(self, parent, child):
         self._call(lib().pa_seq_fork(self._h, parent, child))

@@ -13,11 +13,21 @@
 //     they may be moved to host memory and back: swap-out releases every
 //     block of the sequence and keeps its length, swap-in takes fresh blocks
 //     for the whole length, all or none.
-// The free list is first in, first out; blocks freed together join its tail
-// in logical order.  Every operation validates before it mutates, so a
-// failing call leaves the state unchanged.
+//   * automatic prefix caching: a full prompt block is keyed by a hash of
+//     its tokens and of everything before it (the previous block's key), and
+//     a new sequence whose beginning matches reuses the keyed blocks, which
+//     saves prompt processing, not generation [F55 §后来的做法].  Reuse stops
+//     at the first miss.  A key lookup also compares the stored tokens and
+//     previous key, so only a 64-bit collision of two whole chains could
+//     give a false hit.  A block keeps its key after its last holder frees
+//     it, and loses it when taken for other content.
+// The free list is first in, first out (least recently freed goes first);
+// blocks freed together join its tail in logical order.  It is an intrusive
+// doubly linked list, so a cached block is claimed back from the middle in
+// O(1).  Every operation validates before it mutates, so a failing call
+// leaves the state unchanged.
 #include <algorithm>
-#include <deque>
+#include <cstring>
 #include <new>
 #include <unordered_map>
 #include <vector>
@@ -31,25 +41,73 @@ struct pa_allocator {
   };
   int32_t num_blocks = 0;
   int32_t block_size = 1;
-  std::deque<int32_t> free_list;
+  // free list: intrusive, first in first out
+  std::vector<int32_t> fnext, fprev;
+  std::vector<uint8_t> is_free;
+  int32_t fhead = -1, ftail = -1, nfree = 0;
   std::vector<int32_t> refcount;
+  // prefix cache
+  std::unordered_map<uint64_t, int32_t> cache;  // chain hash -> block
+  std::vector<uint8_t> keyed;
+  std::vector<uint64_t> key_hash, key_parent;
+  std::vector<int32_t> key_tokens;  // [num_blocks][block_size], filled lazily
   std::unordered_map<int32_t, Seq> seqs;
   std::unordered_map<int32_t, int32_t> swapped;  // swapped-out sequence -> its context length
   std::vector<int32_t> arrival;  // first-come order (swapped-out sequences keep their place)
 
   bool exists(int32_t seq) const { return seqs.count(seq) || swapped.count(seq); }
+
+  void push_free(int32_t b) {
+    fprev[b] = ftail;
+    fnext[b] = -1;
+    if (ftail >= 0) fnext[ftail] = b; else fhead = b;
+    ftail = b;
+    is_free[b] = 1;
+    ++nfree;
+  }
+  void unlink_free(int32_t b) {
+    if (fprev[b] >= 0) fnext[fprev[b]] = fnext[b]; else fhead = fnext[b];
+    if (fnext[b] >= 0) fprev[fnext[b]] = fprev[b]; else ftail = fprev[b];
+    is_free[b] = 0;
+    --nfree;
+  }
   void release(int32_t b) {
     refcount[b] -= 1;
-    if (refcount[b] == 0) free_list.push_back(b);
+    if (refcount[b] == 0) push_free(b);
   }
-
+  // The free list's head, for new content: a key it kept is dropped.
   int32_t take() {
-    int32_t b = free_list.front();
-    free_list.pop_front();
+    const int32_t b = fhead;
+    unlink_free(b);
     refcount[b] = 1;
+    if (!keyed.empty() && keyed[b]) {
+      auto it = cache.find(key_hash[b]);
+      if (it != cache.end() && it->second == b) cache.erase(it);
+      keyed[b] = 0;
+    }
     return b;
   }
 };
+
+namespace {
+
+// FNV-1a, 64-bit (Fowler, Noll, Vo): the chain hash of the prefix cache.
+uint64_t fnv1a(uint64_t h, const void* data, size_t n) {
+  const unsigned char* p = static_cast<const unsigned char*>(data);
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 0x100000001b3ull;
+  }
+  return h;
+}
+constexpr uint64_t kFnvBasis = 0xcbf29ce484222325ull;
+
+// Key of a full block: its tokens and the key of the block before it (0 for the first).
+uint64_t block_key(uint64_t parent, const int32_t* tokens, int32_t bs) {
+  return fnv1a(fnv1a(kFnvBasis, &parent, sizeof parent), tokens, sizeof(int32_t) * static_cast<size_t>(bs));
+}
+
+}  // namespace
 
 using pa::fail;
 using pa::ok;
@@ -66,6 +124,9 @@ extern "C" pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
   a->num_blocks = num_blocks;
   a->block_size = block_size;
   a->refcount.assign(num_blocks, 0);
+  a->fnext.assign(num_blocks, -1);
+  a->fprev.assign(num_blocks, -1);
+  a->is_free.assign(num_blocks, 0);
   if (free_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -75,10 +136,10 @@ extern "C" pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
         return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: free_order is not a permutation (entry %d)", i);
       }
       seen[b] = 1;
-      a->free_list.push_back(b);
+      a->push_free(b);
     }
   } else {
-    for (int32_t b = 0; b < num_blocks; ++b) a->free_list.push_back(b);
+    for (int32_t b = 0; b < num_blocks; ++b) a->push_free(b);
   }
   *out = a;
   return ok();
@@ -87,7 +148,7 @@ extern "C" pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
 extern "C" void pa_allocator_destroy(pa_allocator* a) { delete a; }
 
 extern "C" int32_t pa_allocator_num_free(const pa_allocator* a) {
-  return a ? static_cast<int32_t>(a->free_list.size()) : -1;
+  return a ? a->nfree : -1;
 }
 
 extern "C" pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens) {
@@ -95,9 +156,9 @@ extern "C" pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_t
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_allocate: bad argument (seq %d, tokens %d)", seq, num_tokens);
   if (a->exists(seq)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_allocate: sequence %d exists", seq);
   int64_t need = (static_cast<int64_t>(num_tokens) + a->block_size - 1) / a->block_size;
-  if (need > static_cast<int64_t>(a->free_list.size()))
-    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_allocate: sequence %d needs %lld blocks, %zu free", seq,
-                static_cast<long long>(need), a->free_list.size());
+  if (need > a->nfree)
+    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_allocate: sequence %d needs %lld blocks, %d free", seq,
+                static_cast<long long>(need), a->nfree);
   pa_allocator::Seq s;
   s.blocks.reserve(need);
   for (int64_t i = 0; i < need; ++i) s.blocks.push_back(a->take());
@@ -105,6 +166,72 @@ extern "C" pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_t
   a->seqs.emplace(seq, std::move(s));
   a->arrival.push_back(seq);
   return ok();
+}
+
+extern "C" pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const int32_t* tokens,
+                                            int32_t num_tokens, int32_t* num_cached_tokens) {
+  static const char* fn = "pa_seq_allocate_cached";
+  if (!a || seq < 0 || num_tokens < 0 || !num_cached_tokens || (num_tokens > 0 && !tokens))
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: bad argument (seq %d, tokens %d)", fn, seq, num_tokens);
+  if (a->exists(seq)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: sequence %d exists", fn, seq);
+  const int32_t bs = a->block_size;
+  const int64_t need = (static_cast<int64_t>(num_tokens) + bs - 1) / bs;
+  const int64_t full = num_tokens / bs;
+  // chain keys of every full block, and the leading run of cache hits
+  std::vector<uint64_t> keys(full);
+  std::vector<int32_t> hits;
+  uint64_t parent = 0;
+  bool hitting = true;
+  for (int64_t j = 0; j < full; ++j) {
+    const int32_t* t = tokens + j * bs;
+    keys[j] = block_key(parent, t, bs);
+    if (hitting) {
+      auto it = a->cache.find(keys[j]);
+      const int32_t b = it == a->cache.end() ? -1 : it->second;
+      hitting = b >= 0 && a->key_parent[b] == parent &&
+                std::memcmp(&a->key_tokens[static_cast<size_t>(b) * bs], t, sizeof(int32_t) * bs) == 0;
+      if (hitting) hits.push_back(b);
+    }
+    parent = keys[j];
+  }
+  int64_t claimed = 0;
+  for (int32_t b : hits) claimed += a->refcount[b] == 0;
+  if (need - static_cast<int64_t>(hits.size()) + claimed > a->nfree)
+    return fail(PA_ERR_OUT_OF_BLOCKS, "%s: sequence %d needs %lld new blocks, %d free", fn, seq,
+                static_cast<long long>(need - static_cast<int64_t>(hits.size()) + claimed), a->nfree);
+  if (a->keyed.empty()) {
+    a->keyed.assign(a->num_blocks, 0);
+    a->key_hash.assign(a->num_blocks, 0);
+    a->key_parent.assign(a->num_blocks, 0);
+    a->key_tokens.assign(static_cast<size_t>(a->num_blocks) * bs, 0);
+  }
+  pa_allocator::Seq s;
+  s.blocks.reserve(need);
+  for (int32_t b : hits) {
+    if (a->refcount[b] == 0) a->unlink_free(b);
+    a->refcount[b] += 1;
+    s.blocks.push_back(b);
+  }
+  for (int64_t j = static_cast<int64_t>(hits.size()); j < need; ++j) {
+    const int32_t b = a->take();
+    s.blocks.push_back(b);
+    if (j < full && !a->cache.count(keys[j])) {
+      a->cache.emplace(keys[j], b);
+      a->keyed[b] = 1;
+      a->key_hash[b] = keys[j];
+      a->key_parent[b] = j > 0 ? keys[j - 1] : 0;
+      std::memcpy(&a->key_tokens[static_cast<size_t>(b) * bs], tokens + j * bs, sizeof(int32_t) * bs);
+    }
+  }
+  s.ctx = num_tokens;
+  a->seqs.emplace(seq, std::move(s));
+  a->arrival.push_back(seq);
+  *num_cached_tokens = static_cast<int32_t>(hits.size()) * bs;
+  return ok();
+}
+
+extern "C" int32_t pa_prefix_cache_size(const pa_allocator* a) {
+  return a ? static_cast<int32_t>(a->cache.size()) : -1;
 }
 
 extern "C" pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child) {
@@ -129,14 +256,14 @@ extern "C" pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* c
   if (s.ctx == INT32_MAX) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_append_slot: context overflow");
   if (s.ctx % a->block_size == 0) {
     // the last block is full (or there is none): lazily take a new one
-    if (a->free_list.empty())
+    if (a->nfree == 0)
       return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_append_slot: no free block for sequence %d", seq);
     s.blocks.push_back(a->take());
   } else {
     int32_t last = s.blocks.back();
     if (a->refcount[last] > 1) {
       // the slot lies in a partially filled block another sequence holds
-      if (a->free_list.empty())
+      if (a->nfree == 0)
         return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_append_slot: no free block for the copy of block %d", last);
       int32_t dst = a->take();
       a->refcount[last] -= 1;
@@ -192,9 +319,9 @@ extern "C" pa_status pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* block
   *num_blocks = static_cast<int32_t>(need);
   if (need > cap) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_swap_in: %lld blocks, room for %d",
                               static_cast<long long>(need), cap);
-  if (need > static_cast<int64_t>(a->free_list.size()))
-    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_swap_in: sequence %d needs %lld blocks, %zu free", seq,
-                static_cast<long long>(need), a->free_list.size());
+  if (need > a->nfree)
+    return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_swap_in: sequence %d needs %lld blocks, %d free", seq,
+                static_cast<long long>(need), a->nfree);
   pa_allocator::Seq s;
   s.ctx = sw->second;
   for (int64_t i = 0; i < need; ++i) {
@@ -249,7 +376,7 @@ extern "C" int32_t pa_block_refcount(const pa_allocator* a, int32_t block) {
 extern "C" pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out) {
   if (!a || !out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_get_stats: NULL argument");
   out->num_blocks = a->num_blocks;
-  out->num_free = static_cast<int32_t>(a->free_list.size());
+  out->num_free = a->nfree;
   out->num_shared = 0;
   for (int32_t c : a->refcount) out->num_shared += (c > 1);
   out->num_seqs = static_cast<int32_t>(a->seqs.size());

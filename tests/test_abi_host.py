@@ -215,3 +215,77 @@ def test_arrival_simulator_rejects_impossible_inputs():
     with pytest.raises(_lib.PagedAttnError):
         api.simulate_arrivals(4, 4, [0, -1], [3, 3])
     assert api.simulate_arrivals(4, 4, [], [])["rounds"] == 0
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cpp_prefix_cache_matches_reference_exactly(bs, seed):
+    """Prompts drawn from a few shared beginnings plus random tails, mixed with
+    forks, appends, frees and plain allocations: the C++ allocator (chained
+    hashes) and the reference (exact token-prefix keys) reuse the same blocks,
+    report the same cached token counts and keep the same free order."""
+    rng = np.random.default_rng(seed)
+    nb = 48
+    order = rng.permutation(nb)
+    ref, lib_a = OracleAllocator(nb, bs, order), Allocator(nb, bs, order)
+    systems = [rng.integers(0, 4, 4 * bs + 1).tolist() for _ in range(3)]
+    live, nxt = [], 0
+    for _ in range(600):
+        op = int(rng.integers(0, 12))
+        if op < 4 or not live:
+            toks = systems[int(rng.integers(0, 3))][: int(rng.integers(0, 4 * bs + 2))]
+            toks = toks + rng.integers(0, 4, int(rng.integers(0, 2 * bs))).tolist()
+            name, args, new = "allocate_cached", (nxt, toks), nxt
+        elif op < 5:
+            name, args, new = "allocate", (nxt, int(rng.integers(0, 2 * bs + 1))), nxt
+        elif op < 6:
+            name, args, new = "fork", (int(rng.choice(live)), nxt), nxt
+        elif op < 10:
+            name, args, new = "append_slot", (int(rng.choice(live)),), None
+        else:
+            name, args, new = "free_seq", (int(rng.choice(live)),), None
+        r_exc = l_exc = False
+        try:
+            r = getattr(ref, name)(*args)
+        except RefOutOfBlocks:
+            r_exc = True
+        try:
+            l = getattr(lib_a, name)(*args)
+        except OutOfBlocks:
+            l_exc = True
+        assert r_exc == l_exc, (name, args)
+        if not r_exc:
+            assert r == l, (name, args)
+            if new is not None:
+                live.append(new)
+                nxt += 1
+            if name == "free_seq":
+                live.remove(args[0])
+        assert ref.num_free() == lib_a.num_free()
+        assert len(ref.cache) == lib_a.prefix_cache_size()
+        for s in live:
+            assert ref.table(s) == lib_a.table(s)
+        if len(live) > 10:
+            s = live.pop(0)
+            ref.free_seq(s)
+            lib_a.free_seq(s)
+    for b in range(nb):
+        assert lib_a.refcount(b) == ref.refcount[b]
+    # the free lists agree in order: draining them hands out the same blocks
+    n = ref.num_free()
+    ref.allocate(10**6, n * bs)
+    lib_a.allocate(10**6, n * bs)
+    assert ref.table(10**6) == lib_a.table(10**6)
+
+
+def test_prefix_cache_argument_checks():
+    a = Allocator(8, 4)
+    L = _lib.lib()
+    c = ctypes.c_int32(-1)
+    assert L.pa_seq_allocate_cached(a._h, 0, None, 3, ctypes.byref(c)) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_seq_allocate_cached(a._h, 0, None, 0, None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_seq_allocate_cached(a._h, 0, None, 0, ctypes.byref(c)) == _lib.PA_OK and c.value == 0
+    assert a.allocate_cached(1, list(range(9))) == 0 and a.prefix_cache_size() == 2
+    with pytest.raises(_lib.PagedAttnError):
+        a.allocate_cached(1, [1])  # the id is taken
+    assert L.pa_prefix_cache_size(None) == -1
