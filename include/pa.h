@@ -223,6 +223,39 @@ pa_status pa_decode_step(const pa_kv_cache* cache, const void* q, const void* k_
                          int32_t max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/*
+ * pa_decode_shared_prefix — decode (and, with k_new/v_new non-NULL, the
+ * append of pa_decode_step) for batches whose sequences share a prompt
+ * prefix in the same physical blocks (a fork, a common system prompt, a
+ * prefix-cache hit) [F55 §后来的做法, §常见问题];
+ * [IPX §同一提示生成两个回答的假想例子].  The result is the same attention as
+ * pa_decode over each sequence's whole context; only the work differs.
+ * Sequences [group_start[g], group_start[g+1]) (host int32, num_groups + 1
+ * entries, non-decreasing, within [0, num_seqs]) hold the same first
+ * group_shared_blocks[g] (host int32) table entries.  A prefix pass reads
+ * those blocks once per KV head, through the table of the group's first
+ * sequence, for all of the group's (sequence, query head) rows on the matrix
+ * cores, and leaves per-row partials; the decode launch then covers each
+ * sequence's own tokens and merges both exactly.  The caller guarantees the
+ * sharing: entries past the first sequence's are not read for the shared
+ * range.  A sequence whose context is shorter than its group's shared
+ * tokens, or (when appending) whose new token would fall inside them, gets
+ * NaN output.  At most 16 groups; sequences outside every group decode
+ * normally.  Needs f16 activations and an f16 or FP8 pool when any group
+ * shares blocks (else PA_ERR_UNSUPPORTED).  Workspace: at least
+ * pa_decode_shared_workspace_size(num_seqs, num_q_heads, head_dim,
+ * max_context_len, the largest group_shared_blocks * block_size) bytes,
+ * zero-filled before first use (the counters are left at zero).
+ */
+pa_status pa_decode_shared_prefix(const pa_kv_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                  void* out, int32_t act, int32_t num_q_heads, const int32_t* block_tables,
+                                  const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                  int32_t max_context_len, float sm_scale, int32_t num_groups,
+                                  const int32_t* group_start, const int32_t* group_shared_blocks, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+size_t pa_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                       int32_t max_context_len, int32_t max_shared_tokens);
+
 /* ============================== host allocator ============================= */
 /*
  * The block allocator keeps the bookkeeping of [F55 §像内存分页, §块表,

@@ -181,6 +181,41 @@ def decode_step(cache: KVCache, q, k_new, v_new, block_tables, context_lens, max
     return out
 
 
+def shared_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, max_shared_tokens):
+    return int(lib().pa_decode_shared_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                     max_shared_tokens))
+
+
+def decode_shared_prefix(cache: KVCache, q, block_tables, context_lens, max_context_len, sm_scale, group_start,
+                         group_shared_blocks, k_new=None, v_new=None, out=None, workspace=None, stream=None):
+    """Decode (with the append when k_new/v_new are given) of a batch whose sequence groups
+    [group_start[g], group_start[g + 1]) share their first group_shared_blocks[g] blocks
+    (pa_decode_shared_prefix)."""
+    B, hq, d = q.shape
+    act = _act(q)
+    gs = np.ascontiguousarray(group_start, dtype=np.int32)
+    gb = np.ascontiguousarray(group_shared_blocks, dtype=np.int32)
+    if gs.ndim != 1 or gb.ndim != 1 or len(gs) != len(gb) + 1:
+        raise ValueError("group_start needs one more entry than group_shared_blocks")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        shape = (B, cache.num_kv_heads, cache.head_dim)
+        _dev(k_new, q.dtype, "k_new", shape)
+        _dev(v_new, q.dtype, "v_new", shape)
+    if workspace is None:
+        need = shared_workspace_size(B, hq, d, max_context_len, int(gb.max(initial=0)) * cache.block_size)
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    out, workspace, ws_bytes = _decode_args(cache, q, block_tables, context_lens, max_context_len, out, workspace)
+    check(lib().pa_decode_shared_prefix(ctypes.byref(cache.struct), _ptr(q), _ptr(k_new) if k_new is not None else None,
+                                        _ptr(v_new) if v_new is not None else None, _ptr(out), act, hq,
+                                        _ptr(block_tables), _ptr(context_lens), B, block_tables.shape[1],
+                                        int(max_context_len), float(sm_scale), len(gb),
+                                        gs.ctypes.data_as(ctypes.c_void_p), gb.ctypes.data_as(ctypes.c_void_p),
+                                        _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
 def timing_enable(on=True):
     check(lib().pa_timing_enable(1 if on else 0))
 

@@ -2,6 +2,7 @@
 // reading device memory), dispatch to the kernels, and kernel timing.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <map>
 #include <mutex>
@@ -140,13 +141,28 @@ static size_t counters_bytes(int32_t num_seqs, int32_t num_q_heads) {
   return (b + 255) & ~static_cast<size_t>(255);
 }
 
-extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                           int32_t max_context_len) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  const int32_t parts = max_parts_for(max_context_len);
-  if (parts <= 1) return 0;
+static size_t workspace_bytes_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t parts) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || parts <= 1) return 0;
   return counters_bytes(num_seqs, num_q_heads) +
          static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+}
+
+// Partials per (sequence, head) of a shared-prefix decode: the prefix pass's
+// (kPrefixPartTokens each) and the decode launch's (at least
+// kPartitionTokens each).
+static int32_t shared_parts_for(int32_t max_context_len, int32_t max_shared_tokens) {
+  const int32_t pre = max_shared_tokens <= 0 ? 0 : (max_shared_tokens + pa::kPrefixPartTokens - 1) / pa::kPrefixPartTokens;
+  return pre + max_parts_for(max_context_len);
+}
+
+extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                           int32_t max_context_len) {
+  return workspace_bytes_for(num_seqs, num_q_heads, head_dim, max_parts_for(max_context_len));
+}
+
+extern "C" size_t pa_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                                  int32_t max_context_len, int32_t max_shared_tokens) {
+  return workspace_bytes_for(num_seqs, num_q_heads, head_dim, shared_parts_for(max_context_len, max_shared_tokens));
 }
 
 namespace pa {
@@ -175,7 +191,8 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
                         void* out, int32_t act, int32_t num_q_heads, const int32_t* block_tables,
                         const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                         int32_t max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, int32_t num_groups = 0, const int32_t* group_start = nullptr,
+                        const int32_t* group_shared_blocks = nullptr) {
   if (pa_status s = check_cache(cache, fn)) return s;
   if (pa_status s = check_act(cache, act, fn)) return s;
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq < 0 || max_context_len < 0)
@@ -190,10 +207,34 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
   if (max_context_len > pa::kMaxContextLen)
     return fail(PA_ERR_UNSUPPORTED, "%s: max_context_len %d above %d", fn, max_context_len, pa::kMaxContextLen);
   if (!(sm_scale == sm_scale)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: sm_scale is NaN", fn);
+  // shared prefixes: host arrays, checked before anything else is touched
+  int32_t max_shared = 0;
+  if (num_groups < 0 || num_groups > pa::kMaxPrefixGroups)
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d shared-prefix groups (at most %d)", fn, num_groups, pa::kMaxPrefixGroups);
+  if (num_groups > 0) {
+    if (!group_start || !group_shared_blocks) return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL group array", fn);
+    if (group_start[0] < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: group_start[0] = %d", fn, group_start[0]);
+    for (int32_t g = 0; g < num_groups; ++g) {
+      if (group_start[g + 1] < group_start[g] || group_start[g + 1] > num_seqs)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: group %d spans sequences [%d, %d) of %d", fn, g, group_start[g],
+                    group_start[g + 1], num_seqs);
+      const int64_t tok = static_cast<int64_t>(group_shared_blocks[g]) * cache->block_size;
+      if (group_shared_blocks[g] < 0 || group_shared_blocks[g] > max_blocks_per_seq || tok > max_context_len)
+        return fail(PA_ERR_INVALID_ARGUMENT, "%s: group %d shares %d blocks (max blocks %d, max context %d)", fn, g,
+                    group_shared_blocks[g], max_blocks_per_seq, max_context_len);
+      max_shared = std::max<int32_t>(max_shared, static_cast<int32_t>(tok));
+    }
+    if (max_shared > 0 && (act != PA_F16 || cache->kv_dtype == PA_F32))
+      return fail(PA_ERR_UNSUPPORTED, "%s: shared prefixes need f16 activations and an f16 or FP8 pool", fn);
+    if (shared_parts_for(max_context_len, max_shared) > pa::kMaxPartitions)
+      return fail(PA_ERR_UNSUPPORTED, "%s: %d partials per head (at most %d)", fn,
+                  shared_parts_for(max_context_len, max_shared), pa::kMaxPartitions);
+  }
   if (num_seqs == 0) return ok();
   if (!q || !out || !block_tables || !context_lens || (k_new == nullptr) != (v_new == nullptr))
     return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL device pointer", fn);
-  const size_t need = pa_decode_workspace_size(num_seqs, num_q_heads, cache->head_dim, max_context_len);
+  const int32_t parts = max_shared > 0 ? shared_parts_for(max_context_len, max_shared) : max_parts_for(max_context_len);
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, cache->head_dim, parts);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
 
@@ -210,8 +251,25 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
   a.num_seqs = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.max_ctx = max_context_len;
-  a.max_parts = max_parts_for(max_context_len);
+  a.max_parts = parts;
   a.sm_scale = sm_scale;
+  if (max_shared > 0) {
+    a.ngroups = num_groups;
+    for (int32_t g = 0; g <= num_groups; ++g) a.gstart[g] = group_start[g];
+    for (int32_t g = 0; g < num_groups; ++g) {
+      a.gtok[g] = group_shared_blocks[g] * cache->block_size;
+      a.gparts[g] = (a.gtok[g] + pa::kPrefixPartTokens - 1) / pa::kPrefixPartTokens;
+    }
+    // every sequence skips at least min_begin tokens when the groups cover
+    // the whole batch (a sequence of no group skips none)
+    int32_t covered = 0, min_begin = INT32_MAX;
+    for (int32_t g = 0; g < num_groups; ++g) {
+      const int32_t n = group_start[g + 1] - group_start[g];
+      covered += n;
+      if (n > 0) min_begin = std::min(min_begin, a.gtok[g]);
+    }
+    a.min_begin = covered == num_seqs && min_begin != INT32_MAX ? min_begin : 0;
+  }
   if (need > 0) {
     char* base = static_cast<char*>(workspace);
     a.counters = reinterpret_cast<int*>(base);
@@ -224,7 +282,14 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
     a.ev[0] = g_timing.part_ev[2 * g_timing.n_part];
     a.ev[1] = g_timing.part_ev[2 * g_timing.n_part + 1];
   }
-  const hipError_t e = pa::launch_decode(a);
+  hipError_t e = hipSuccess;
+  if (a.ngroups > 0) {
+    // the prefix pass first (the timing brackets both launches)
+    if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
+    a.ev[0] = nullptr;
+    e = pa::launch_prefix_pass(a);
+  }
+  if (e == hipSuccess) e = pa::launch_decode(a);
   if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "%s: unsupported dtype/shape combination", fn);
   if (timed && e == hipSuccess) g_timing.n_part += 1;
   return hip_status(e, fn);
@@ -249,6 +314,18 @@ extern "C" pa_status pa_decode_step(const pa_kv_cache* cache, const void* q, con
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_step: k_new/v_new is NULL");
   return decode_common("pa_decode_step", cache, q, k_new, v_new, out, act, num_q_heads, block_tables, context_lens,
                        num_seqs, max_blocks_per_seq, max_context_len, sm_scale, workspace, workspace_bytes, stream);
+}
+
+extern "C" pa_status pa_decode_shared_prefix(const pa_kv_cache* cache, const void* q, const void* k_new,
+                                             const void* v_new, void* out, int32_t act, int32_t num_q_heads,
+                                             const int32_t* block_tables, const int32_t* context_lens,
+                                             int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                             float sm_scale, int32_t num_groups, const int32_t* group_start,
+                                             const int32_t* group_shared_blocks, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  return decode_common("pa_decode_shared_prefix", cache, q, k_new, v_new, out, act, num_q_heads, block_tables,
+                       context_lens, num_seqs, max_blocks_per_seq, max_context_len, sm_scale, workspace,
+                       workspace_bytes, stream, num_groups, group_start, group_shared_blocks);
 }
 
 extern "C" pa_status pa_timing_enable(int32_t on) {

@@ -191,11 +191,17 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   const int log2_bs = P.log2_bs;
   const int bs = 1 << log2_bs;
   const int ctx = P.ctx[s];
-  const bool bad_len =
-      ctx < 0 || ctx > P.max_ctx || static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) * bs;
-  const int nparts = bad_len ? 1 : max(1, (ctx + PART - 1) / PART);
+  // A shared prefix's tokens [0, begin) were covered by the prefix pass, which
+  // left `pre` partials; the new token may not lie in them.
+  const SeqPrefix pf = seq_prefix(P, s);
+  const bool bad_len = ctx < 0 || ctx > P.max_ctx ||
+                       static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) * bs || ctx < pf.begin ||
+                       (P.k_new != nullptr && pf.pre > 0 && ctx - 1 < pf.begin);
+  // this launch's partitions; partition 0 starts from the prefix's merged
+  // state, so these are all the partials to merge
+  const int nparts = bad_len ? 1 : max(1, (ctx - pf.begin + PART - 1) / PART);
   if (p >= nparts) return;
-  const int t0 = p * PART;
+  const int t0 = (bad_len ? 0 : pf.begin) + p * PART;
   const int t1 = bad_len ? t0 : min(t0 + PART, ctx);
   const int b0 = t0 >> log2_bs;
   const int64_t trow = static_cast<int64_t>(s) * P.max_blocks;
@@ -269,6 +275,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  // a shared prefix's partials enter through one row of lanes of partition 0
+  if (p == 0 && pf.pre > 0 && !bad_early && w == 0 && row == 0)
+    load_prefix_state<D, EPL>(P, sh, pf.pre, c * EPL, m, l, acc);
 
   const int nrounds = bad_early ? 0 : (t1 - t0 + ROUND - 1) / ROUND;
   for (int r0 = 0; r0 < nrounds; r0 += U) {
@@ -367,10 +376,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
     if (nparts == 1) {
       out[sh * D + i] = from_f32<ACT>(bad_early ? NAN : (ctx > 0 ? o / L * P.v_scale : 0.f));
     } else {
-      coherent_store(&P.ws_o[(sh * P.max_parts + p) * D + i], o * P.v_scale);
+      const int slot = pf.pre + p;
+      coherent_store(&P.ws_o[(sh * P.max_parts + slot) * D + i], o * P.v_scale);
       if (i == 0) {
-        coherent_store(&P.ws_ml[(sh * P.max_parts + p) * 2], mx);
-        coherent_store(&P.ws_ml[(sh * P.max_parts + p) * 2 + 1], L);
+        coherent_store(&P.ws_ml[(sh * P.max_parts + slot) * 2], mx);
+        coherent_store(&P.ws_ml[(sh * P.max_parts + slot) * 2 + 1], L);
       }
     }
   }
@@ -389,7 +399,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   __syncthreads();
   if (!is_last) return;
   __shared__ float merge_m[kMergeCap], merge_w[kMergeCap];
-  merge_partials<ACT, D, NW * 64>(P, sh, 1, nparts, tid, merge_m, merge_w);
+  merge_partials<ACT, D, NW * 64>(P, sh, 1, pf.pre, nparts, tid, merge_m, merge_w);
   if (tid == 0) __hip_atomic_store(&P.counters[sh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -399,7 +409,7 @@ hipError_t decode_t(const DecodeArgs& a) {
   constexpr int TPL = 64 / (D / Math<KV, ACT>::EPL);
   const pa_kv_cache& c = *a.cache;
   const DecodeParams P = make_decode_params(a);
-  const unsigned np = static_cast<unsigned>(a.max_parts);
+  const unsigned np = static_cast<unsigned>(decode_grid_parts(a, kPartitionTokens));
   const dim3 grid(PA_GRID_HEAD_FIRST ? a.num_q_heads : np, PA_GRID_HEAD_FIRST ? np : a.num_q_heads, a.num_seqs);
   auto kern = c.block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true> : decode_kernel<KV, ACT, D, NW, U, false>;
   if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);

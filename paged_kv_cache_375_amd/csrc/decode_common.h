@@ -33,7 +33,26 @@ struct DecodeParams {
   // scores are kept in log2 units: score_scale = sm_scale * log2(e) (* k_scale
   // for FP8 pools); v_scale multiplies the output (FP8 pools, else 1)
   float score_scale, v_scale, k_inv, v_inv;
+  // shared prefixes (DecodeArgs): a sequence of group g starts this launch's
+  // tokens at gtok[g] and finds gparts[g] prefix partials in slots 0.. of
+  // its workspace rows; gwg[g] = first prefix-pass workgroup of group g
+  int ngroups;
+  int gstart[kMaxPrefixGroups + 1];
+  int gtok[kMaxPrefixGroups];
+  int gparts[kMaxPrefixGroups];
+  int gwg[kMaxPrefixGroups + 1];
 };
+
+// Where sequence s's own tokens begin, and how many prefix partials precede
+// its partitions' slots (both 0 outside every shared-prefix group).
+struct SeqPrefix {
+  int begin, pre;
+};
+__device__ __forceinline__ SeqPrefix seq_prefix(const DecodeParams& P, int s) {
+  for (int g = 0; g < P.ngroups; ++g)
+    if (s >= P.gstart[g] && s < P.gstart[g + 1]) return SeqPrefix{P.gtok[g], P.gparts[g]};
+  return SeqPrefix{0, 0};
+}
 
 inline DecodeParams make_decode_params(const DecodeArgs& a) {
   const pa_kv_cache& c = *a.cache;
@@ -64,6 +83,15 @@ inline DecodeParams make_decode_params(const DecodeArgs& a) {
   P.v_scale = c.kv_dtype == PA_FP8_E4M3 ? c.v_scale : 1.f;
   P.k_inv = c.k_inv_scale;
   P.v_inv = c.v_inv_scale;
+  P.ngroups = a.ngroups;
+  for (int g = 0; g <= kMaxPrefixGroups; ++g) {
+    P.gstart[g] = g <= a.ngroups ? a.gstart[g] : 0;
+    P.gwg[g] = 0;
+  }
+  for (int g = 0; g < kMaxPrefixGroups; ++g) {
+    P.gtok[g] = g < a.ngroups ? a.gtok[g] : 0;
+    P.gparts[g] = g < a.ngroups ? a.gparts[g] : 0;
+  }
   return P;
 }
 
@@ -123,13 +151,39 @@ __device__ __forceinline__ void store_new_token(const DecodeParams& P, int s, in
 
 namespace pa {
 
+// The merged state of a shared prefix: the prefix pass left `pre` partials
+// of workspace row sh in slots 0 .. pre - 1, each (m, l) and an unnormalised
+// vector (without the V scale).  Returns the running max M (log2 units), the
+// weight sum L and elements [d0, d0 + N) of the vector, rescaled to M; a
+// decode partition starts its online softmax from them.  Coherent loads:
+// another launch wrote the partials, possibly from another XCD.
+template <int D, int N>
+__device__ __forceinline__ void load_prefix_state(const DecodeParams& P, int64_t sh, int pre, int d0, float& M,
+                                                  float& L, float* o) {
+  const float* ml = P.ws_ml + sh * P.max_parts * 2;
+  M = -INFINITY;
+  for (int q = 0; q < pre; ++q) M = fmaxf(M, coherent_load(ml + 2 * q));
+  const float mu = M == -INFINITY ? 0.f : M;
+  L = 0.f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) o[e] = 0.f;
+  for (int q = 0; q < pre; ++q) {
+    const float w = exp2f(coherent_load(ml + 2 * q) - mu);
+    L += w * coherent_load(ml + 2 * q + 1);
+    const float* src = P.ws_o + (sh * P.max_parts + q) * D + d0;
+#pragma unroll
+    for (int e = 0; e < N; ++e) o[e] += w * coherent_load(src + e);
+  }
+}
+
 // Floats of LDS scratch merge_partials needs (two arrays of this size); at
 // least the largest partition count.
 constexpr int kMergeCap = kMaxPartitions;
 
 // The exact merge of split-context partials, run by the last workgroup of a
 // (sequence, head group) to finish: heads sh0 .. sh0 + nh - 1 (rows of the
-// [num_seqs * hq] workspace), nparts partitions each.  Every partition p
+// [num_seqs * hq] workspace), nparts partitions each, in workspace slots
+// slot0 .. slot0 + nparts - 1.  Every partition p
 // left (m_p, l_p) (running max in log2 units and weight sum) and the
 // unnormalised vector o_p; the result is
 //   out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p,
@@ -139,15 +193,15 @@ constexpr int kMergeCap = kMaxPartitions;
 // scratch of kMergeCap floats each.  NT threads take part; the caller
 // synchronises before the call.
 template <typename ACT, int D, int NT>
-__device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh0, int nh, int nparts, int tid,
-                                               float* mw, float* ww) {
+__device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh0, int nh, int slot0, int nparts,
+                                               int tid, float* mw, float* ww) {
   ACT* out = static_cast<ACT*>(P.out);
   const int hb = max(1, min(nh, kMergeCap / nparts));  // heads per batch
   for (int hbase = 0; hbase < nh; hbase += hb) {
     const int nb = min(hb, nh - hbase);
     for (int i = tid; i < nb * nparts; i += NT) {
       const int hh = i / nparts, q = i - hh * nparts;
-      const float* ml = P.ws_ml + ((sh0 + hbase + hh) * P.max_parts + q) * 2;
+      const float* ml = P.ws_ml + ((sh0 + hbase + hh) * P.max_parts + slot0 + q) * 2;
       mw[i] = coherent_load(ml);
       ww[i] = coherent_load(ml + 1);
     }
@@ -169,7 +223,7 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh
     for (int i = tid; i < nb * (D / 4); i += NT) {
       const int hh = i / (D / 4), d = (i - hh * (D / 4)) * 4;
       const int64_t sh = sh0 + hbase + hh;
-      const float* o = P.ws_o + sh * P.max_parts * D + d;
+      const float* o = P.ws_o + (sh * P.max_parts + slot0) * D + d;
       const float* w = ww + hh * nparts;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
       int q = 0;

@@ -39,6 +39,7 @@
 // adjacent [F55 §块表]; [IPX §分离逻辑顺序与实际存储位置].
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "decode_common.h"
@@ -114,34 +115,81 @@ struct Layout {
   static __device__ __forceinline__ int swz_v(int r) { return (2 * r) & (LCH - 2); }
 };
 
-template <typename KV, int D, int HT, int NW, bool UNI>
+// PREFIX = false: decode, one workgroup per (KV head and group of query
+// heads, partition, sequence), as described above.
+// PREFIX = true: the prefix pass of a shared-prefix decode.  The query rows
+// of a workgroup are (sequence, query head) pairs of one group of sequences
+// that share their first gtok tokens (whole blocks) and one KV head, up to
+// 16 * HT of them; the shared blocks, read through the table of the group's
+// first sequence, are loaded once for all of those rows.  Each partition of
+// kPrefixPartTokens tokens leaves (m, l, o) partials in workspace slot p of
+// every row (o without the V scale); the first partition of the decode
+// launch that follows starts its online softmax from their merged state.
+template <typename KV, int D, int HT, int NW, bool UNI, bool PREFIX>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_occupancy<D, HT>()))) void decode_group_kernel(const DecodeParams P, int groups_per_kv) {
   using L = Layout<KV, D>;
   constexpr int KVB = L::KVB, NS = L::NS, NDT = L::NDT, NV = L::NV, LCH = L::LCH;
   constexpr int VCH = L::VCH;
   constexpr int MREGS = HT * NDT * 4 + 2 * HT;  // floats per lane in a wave's partial result
 
-  const int grp = blockIdx.x % groups_per_kv;
-  const int kvh = blockIdx.x / groups_per_kv;
-  const int p = blockIdx.y;
-  const int s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int log2_bs = P.log2_bs;
   const int bs = 1 << log2_bs;
-  const int ctx = P.ctx[s];
-  const bool bad_len =
-      ctx < 0 || ctx > P.max_ctx || static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) * bs;
-  const int part = P.part_tokens;  // a multiple of kPartitionTokens, chosen per launch
-  const int nparts = bad_len ? 1 : max(1, (ctx + part - 1) / part);
-  if (p >= nparts) return;
-  const int t0 = p * part;
-  const int t1 = bad_len ? t0 : min(t0 + part, ctx);
+  int kvh, p, s, ctx, nparts, t0, t1, h0, nh, grp = 0;
+  bool bad_len;
+  SeqPrefix pf{0, 0};
+  int gs = 0, r0 = 0;  // prefix pass: the group's first sequence, the workgroup's first row
+  if constexpr (PREFIX) {
+    const int bx = blockIdx.x;
+    int gi = 0;
+    while (gi + 1 < P.ngroups && bx >= P.gwg[gi + 1]) ++gi;
+    const int rowsets = (P.gwg[gi + 1] - P.gwg[gi]) / P.hkv;
+    kvh = (bx - P.gwg[gi]) / rowsets;
+    r0 = ((bx - P.gwg[gi]) % rowsets) * HT * 16;
+    gs = P.gstart[gi];
+    s = gs;
+    p = blockIdx.y;
+    if (p >= P.gparts[gi]) return;
+    ctx = P.gtok[gi];
+    bad_len = false;
+    nparts = P.gparts[gi];
+    t0 = p * kPrefixPartTokens;
+    t1 = min(t0 + kPrefixPartTokens, ctx);
+    h0 = 0;
+    nh = min(HT * 16, (P.gstart[gi + 1] - gs) * P.group - r0);
+  } else {
+    grp = blockIdx.x % groups_per_kv;
+    kvh = blockIdx.x / groups_per_kv;
+    p = blockIdx.y;
+    s = blockIdx.z;
+    ctx = P.ctx[s];
+    // tokens [0, begin) of a shared prefix were covered by the prefix pass
+    pf = seq_prefix(P, s);
+    bad_len = ctx < 0 || ctx > P.max_ctx || static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) * bs ||
+              ctx < pf.begin || (P.k_new != nullptr && pf.pre > 0 && ctx - 1 < pf.begin);
+    const int part = P.part_tokens;  // a multiple of kPartitionTokens, chosen per launch
+    // this launch's partitions; partition 0 starts from a shared prefix's
+    // merged state, so these are all the partials to merge
+    nparts = bad_len ? 1 : max(1, (ctx - pf.begin + part - 1) / part);
+    if (p >= nparts) return;
+    t0 = (bad_len ? 0 : pf.begin) + p * part;
+    t1 = bad_len ? t0 : min(t0 + part, ctx);
+    h0 = kvh * P.group + grp * HT * 16;          // first query head of the workgroup
+    nh = min(HT * 16, P.group - grp * HT * 16);  // query heads of the workgroup
+  }
+  // workspace row of the workgroup's query row hh
+  auto row_sh = [&](int hh) -> int64_t {
+    if constexpr (PREFIX) {
+      const int R = r0 + hh;
+      return static_cast<int64_t>(gs + R / P.group) * P.hq + kvh * P.group + R % P.group;
+    } else {
+      return static_cast<int64_t>(s) * P.hq + h0 + hh;
+    }
+  };
   const int b0 = t0 >> log2_bs;
   const int64_t trow = static_cast<int64_t>(s) * P.max_blocks;
-  const int h0 = kvh * P.group + grp * HT * 16;              // first query head of the workgroup
-  const int nh = min(HT * 16, P.group - grp * HT * 16);      // query heads of the workgroup
   const int64_t head_rows = static_cast<int64_t>(kvh) * bs;  // token rows before head kvh in a block
   const int64_t block_rows = static_cast<int64_t>(P.hkv) * bs;
 
@@ -169,13 +217,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   // Fused append: the workgroup of the KV head's first query group stores the
   // new token into its slot; every workgroup reading the new token takes it
   // from the caller's rows instead of the pool.
-  const bool has_new = P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
+  const bool has_new = !PREFIX && P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
   if (has_new && grp == 0 && w == 0) store_new_token<KV, half_t, D>(P, s, kvh, ctx, lane);
   for (int i = tid; i < HT * 16 * LCH; i += NW * 64) {
     const int hh = i / LCH, ch = i % LCH;
     uint4 x = make_uint4(0, 0, 0, 0);
-    if (hh < nh) x = *reinterpret_cast<const uint4*>(static_cast<const half_t*>(P.q) +
-                                                     (static_cast<int64_t>(s) * P.hq + h0 + hh) * D + ch * 8);
+    if (hh < nh) x = *reinterpret_cast<const uint4*>(static_cast<const half_t*>(P.q) + row_sh(hh) * D + ch * 8);
     qs[hh * LCH + (ch ^ L::swz_k(hh))] = x;
   }
   if (has_new && tid < 2 * VCH) {
@@ -201,6 +248,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
     lsum[ht] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[ht][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // A shared prefix's partials enter through wave 0 of partition 0: lane
+  // (g, n) takes head column n's max and elements 16 dt + 4 g + i, and the
+  // weight sum goes to the g = 0 lanes (the four lane groups' sums are added
+  // at the end).
+  if constexpr (!PREFIX) {
+    if (p == 0 && pf.pre > 0 && !bad && w == 0) {
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        const int hh = 16 * ht + n;
+        if (hh >= nh) continue;
+        const int64_t sh = row_sh(hh);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          float M, L, v[4];
+          load_prefix_state<D, 4>(P, sh, pf.pre, 16 * dt + 4 * g, M, L, v);
+          m[ht] = M;
+          lsum[ht] = g == 0 ? L : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[ht][dt][i] = v[i];
+        }
+      }
+    }
   }
 
   uint4* const vb = vbuf + w * (kChunk * LCH);
@@ -425,36 +496,50 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   }
 
   half_t* out = static_cast<half_t*>(P.out);
+  // the prefix pass always leaves partials (slot p); decode leaves the output
+  // itself when it is the head's only partition, else partials after the
+  // prefix's
+  const bool direct = !PREFIX && nparts == 1;
+  const int slot = PREFIX ? p : pf.pre + p;
   if (w == 0) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const int hh = 16 * ht + n;
       if (hh >= nh) continue;
-      const int64_t sh = static_cast<int64_t>(s) * P.hq + h0 + hh;
+      const int64_t sh = row_sh(hh);
       const float mx = bad ? NAN : m[ht];
       const float lx = bad ? NAN : lsum[ht];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int d = 16 * dt + 4 * g;
-        if (nparts == 1) {
+        if (direct) {
           const float f = bad ? NAN : (ctx > 0 ? P.v_scale / lx : 0.f);
           half4_t r;
 #pragma unroll
           for (int i = 0; i < 4; ++i) r[i] = static_cast<_Float16>(bad ? NAN : o[ht][dt][i] * f);
           *reinterpret_cast<half4_t*>(out + sh * D + d) = r;
+        } else if (PREFIX) {
+          // read by a later launch: plain 16-byte stores, without the V scale
+          const float4_t nan4 = {NAN, NAN, NAN, NAN};
+          *reinterpret_cast<float4_t*>(P.ws_o + (sh * P.max_parts + slot) * D + d) = bad ? nan4 : o[ht][dt];
         } else {
-          float* dst = P.ws_o + (sh * P.max_parts + p) * D + d;
+          float* dst = P.ws_o + (sh * P.max_parts + slot) * D + d;
 #pragma unroll
           for (int i = 0; i < 4; ++i) coherent_store(dst + i, bad ? NAN : o[ht][dt][i] * P.v_scale);
         }
       }
-      if (nparts > 1 && g == 0) {
-        coherent_store(&P.ws_ml[(sh * P.max_parts + p) * 2], mx);
-        coherent_store(&P.ws_ml[(sh * P.max_parts + p) * 2 + 1], lx);
+      if (!direct && g == 0) {
+        if constexpr (PREFIX) {
+          P.ws_ml[(sh * P.max_parts + slot) * 2] = mx;
+          P.ws_ml[(sh * P.max_parts + slot) * 2 + 1] = lx;
+        } else {
+          coherent_store(&P.ws_ml[(sh * P.max_parts + slot) * 2], mx);
+          coherent_store(&P.ws_ml[(sh * P.max_parts + slot) * 2 + 1], lx);
+        }
       }
     }
   }
-  if (nparts == 1) return;
+  if (direct || PREFIX) return;
 
   // Split context: the last partition to finish merges every partial of the
   // workgroup's heads exactly and restores the arrival counter to zero (see
@@ -468,7 +553,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   if (!is_last) return;
   // the V staging buffers are free now: they hold the merge's scratch
   float* scratch = reinterpret_cast<float*>(vbuf);
-  merge_partials<half_t, D, NW * 64>(P, static_cast<int64_t>(s) * P.hq + h0, nh, nparts, tid, scratch,
+  merge_partials<half_t, D, NW * 64>(P, static_cast<int64_t>(s) * P.hq + h0, nh, pf.pre, nparts, tid, scratch,
                                      scratch + kMergeCap);
   if (tid == 0) __hip_atomic_store(&P.counters[cidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -483,8 +568,8 @@ constexpr int max_head_tiles() {
 template <typename KV, int D, int HT>
 hipError_t launch_ht(const DecodeArgs& a, int groups) {
   constexpr int NW = PA_GROUP_WAVES;
-  auto kern = a.cache->block_size >= 16 ? decode_group_kernel<KV, D, HT, NW, true>
-                                        : decode_group_kernel<KV, D, HT, NW, false>;
+  auto kern = a.cache->block_size >= 16 ? decode_group_kernel<KV, D, HT, NW, true, false>
+                                        : decode_group_kernel<KV, D, HT, NW, false, false>;
   // Partition length: the shortest multiple of kPartitionTokens (doubling)
   // whose worst-case workgroup count fits the GPU's resident slots, so the
   // whole launch runs as one round; when even one partition per unit does
@@ -493,18 +578,19 @@ hipError_t launch_ht(const DecodeArgs& a, int groups) {
   const int64_t units = static_cast<int64_t>(a.cache->num_kv_heads) * groups * a.num_seqs;
   const int slots = resident_slots(reinterpret_cast<const void*>(kern), NW * 64);
   const int64_t cap = static_cast<int64_t>(kTabEntries) * a.cache->block_size;
+  const int64_t span = a.max_ctx - a.min_begin;  // the longest run of a sequence's own tokens
   int part = kPartitionTokens;
   for (int64_t pp = kPartitionTokens; pp <= cap; pp *= 2) {
-    const int64_t parts = (a.max_ctx + pp - 1) / pp;
+    const int64_t parts = (span + pp - 1) / pp;
     if (units * (parts > 0 ? parts : 1) <= slots) {
       part = static_cast<int>(pp);
       break;
     }
-    if (pp >= a.max_ctx) break;
+    if (pp >= span) break;
   }
   DecodeParams P = make_decode_params(a);
   P.part_tokens = part;
-  const int grid_parts = a.max_ctx <= 0 ? 1 : (a.max_ctx + part - 1) / part;
+  const int grid_parts = decode_grid_parts(a, part);
   const dim3 grid(static_cast<unsigned>(a.cache->num_kv_heads * groups), static_cast<unsigned>(grid_parts),
                   static_cast<unsigned>(a.num_seqs));
   if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
@@ -535,6 +621,60 @@ hipError_t launch_d(const DecodeArgs& a) {
   return hipErrorInvalidValue;
 }
 
+// The prefix pass: rows = (sequence, query head) pairs of a group per KV
+// head, in tiles of 16 * HT.
+template <typename KV, int D, int HT>
+hipError_t launch_prefix_ht(const DecodeArgs& a) {
+  constexpr int NW = PA_GROUP_WAVES;
+  auto kern = a.cache->block_size >= 16 ? decode_group_kernel<KV, D, HT, NW, true, true>
+                                        : decode_group_kernel<KV, D, HT, NW, false, true>;
+  DecodeParams P = make_decode_params(a);
+  const int G = a.num_q_heads / a.cache->num_kv_heads;
+  int max_parts = 0;
+  P.gwg[0] = 0;
+  for (int g = 0; g < a.ngroups; ++g) {
+    const int rows = (a.gstart[g + 1] - a.gstart[g]) * G;
+    const int rowsets = a.gparts[g] > 0 ? (rows + 16 * HT - 1) / (16 * HT) : 0;
+    P.gwg[g + 1] = P.gwg[g] + a.cache->num_kv_heads * rowsets;
+    max_parts = a.gparts[g] > max_parts ? a.gparts[g] : max_parts;
+  }
+  if (P.gwg[a.ngroups] == 0 || max_parts == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(P.gwg[a.ngroups]), static_cast<unsigned>(max_parts), 1);
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, a.stream, P, 1);
+  return hipGetLastError();
+}
+
+template <typename KV, int D>
+hipError_t launch_prefix_d(const DecodeArgs& a) {
+  constexpr int HTMAX = max_head_tiles<D>();
+  const int G = a.num_q_heads / a.cache->num_kv_heads;
+  int rows = 0;
+  for (int g = 0; g < a.ngroups; ++g) rows = std::max(rows, (a.gstart[g + 1] - a.gstart[g]) * G);
+  const int ht = std::min(HTMAX, std::max(1, (rows + 15) / 16));
+  switch (ht) {
+    case 1: return launch_prefix_ht<KV, D, 1>(a);
+    case 2: return launch_prefix_ht<KV, D, 2>(a);
+  }
+  if constexpr (HTMAX >= 5) {
+    switch (ht) {
+      case 3: return launch_prefix_ht<KV, D, 3>(a);
+      case 4: return launch_prefix_ht<KV, D, 4>(a);
+      case 5: return launch_prefix_ht<KV, D, 5>(a);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename KV>
+hipError_t launch_prefix_kv(const DecodeArgs& a) {
+  switch (a.cache->head_dim) {
+    case 32: return launch_prefix_d<KV, 32>(a);
+    case 64: return launch_prefix_d<KV, 64>(a);
+    case 128: return launch_prefix_d<KV, 128>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename KV>
 hipError_t launch_kv(const DecodeArgs& a) {
   switch (a.cache->head_dim) {
@@ -555,6 +695,13 @@ bool group_decode_applies(const DecodeArgs& a) {
 hipError_t launch_decode_group(const DecodeArgs& a) {
   if (a.cache->kv_dtype == PA_F16) return launch_kv<half_t>(a);
   if (a.cache->kv_dtype == PA_FP8_E4M3) return launch_kv<fp8_t>(a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefix_pass(const DecodeArgs& a) {
+  if (a.act != PA_F16) return hipErrorInvalidValue;
+  if (a.cache->kv_dtype == PA_F16) return launch_prefix_kv<half_t>(a);
+  if (a.cache->kv_dtype == PA_FP8_E4M3) return launch_prefix_kv<fp8_t>(a);
   return hipErrorInvalidValue;
 }
 

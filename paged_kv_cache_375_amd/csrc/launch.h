@@ -27,6 +27,12 @@ hipError_t launch_copy_blocks(const pa_kv_cache& c, const int32_t* pairs, int n,
 hipError_t launch_swap_blocks(const pa_kv_cache& c, void* host_k, void* host_v, const int32_t* ids, int n,
                               bool to_host, hipStream_t st);
 
+// Shared prefixes (see pa_decode_shared_prefix): at most this many groups
+// per call; the prefix pass splits each prefix into partitions of
+// kPrefixPartTokens tokens.
+constexpr int kMaxPrefixGroups = 16;
+constexpr int kPrefixPartTokens = 256;
+
 struct DecodeArgs {
   const pa_kv_cache* cache;
   const void* q;
@@ -47,7 +53,22 @@ struct DecodeArgs {
   float* ws_o;     // [num_seqs][num_q_heads][max_parts][head_dim]: unnormalised output
   hipStream_t stream;
   hipEvent_t ev[2];  // optional timing events around the kernel (or null)
+  // shared prefixes: sequences [gstart[g], gstart[g+1]) share their first
+  // gtok[g] tokens (whole blocks), whose partials a prefix pass leaves in
+  // workspace slots [0, gparts[g]); ngroups = 0 for plain decode
+  int ngroups;
+  int gstart[kMaxPrefixGroups + 1];
+  int gtok[kMaxPrefixGroups];
+  int gparts[kMaxPrefixGroups];
+  int min_begin;  // the fewest shared tokens of any sequence (0 if one is in no group)
 };
+
+// Partitions of `part` tokens the decode grid needs: the longest context
+// less the shared tokens every sequence skips.
+inline int decode_grid_parts(const DecodeArgs& a, int part) {
+  const int span = a.max_ctx - a.min_begin;
+  return span <= 0 ? 1 : (span + part - 1) / part;
+}
 
 // Table entries a decode workgroup stages in LDS: a partition spans at most
 // kTabEntries blocks.
@@ -65,5 +86,9 @@ hipError_t launch_decode(const DecodeArgs& a);
 // FP8 pools when several query heads share each KV head.
 bool group_decode_applies(const DecodeArgs& a);
 hipError_t launch_decode_group(const DecodeArgs& a);
+// The prefix pass of a shared-prefix decode (f16 activations; f16 or FP8
+// pools): every group's shared tokens, read once per KV head for all of the
+// group's query rows, leave partials in the workspace.
+hipError_t launch_prefix_pass(const DecodeArgs& a);
 
 }  // namespace pa

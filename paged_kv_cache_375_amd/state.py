@@ -8,6 +8,10 @@ copies made while sequences grew, then each sequence's own tokens).
 ``DecodeStep.run()`` is one step of the hot path: the step's copy-on-write
 copies (if any), the append of every sequence's new K/V, and the decode —
 by default the append and the decode share one launch (pa_decode_step).
+With ``shared=True`` on a workload whose sequences fork one prefix, the
+prefix's full blocks, which every table holds in common, go through the
+shared-prefix path (pa_decode_shared_prefix): read once per KV head for all
+sequences, then each sequence's own tokens.
 """
 import math
 
@@ -54,13 +58,30 @@ class DecodeStep:
         self.sm_scale = float(np.float32(1.0 / math.sqrt(wl.head_dim)))
         self.out = torch.empty_like(self.q)
         self.workspace = api.new_workspace(wl.batch, wl.num_q_heads, wl.head_dim, self.max_ctx, device)
+        # full prefix blocks: every sequence's table starts with them (a
+        # partial last prefix block is each sequence's own after copy-on-write)
+        self.shared_blocks = P // wl.block_size
+        self.shared_workspace = None
+        if self.shared_blocks:
+            assert (sc.tables[:, : self.shared_blocks] == sc.tables[0, : self.shared_blocks]).all()
+            need = api.shared_workspace_size(wl.batch, wl.num_q_heads, wl.head_dim, self.max_ctx,
+                                             self.shared_blocks * wl.block_size)
+            self.shared_workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
 
-    def run(self, cache=None, stream=None, fused=True):
-        """One step: copy-on-write copies, then append + decode (one launch when fused)."""
+    def run(self, cache=None, stream=None, fused=True, shared=False):
+        """One step: copy-on-write copies, then append + decode (one launch when fused;
+        a prefix pass first when shared and the workload has a shared prefix)."""
         c = cache or self.cache
         if self.step_pairs is not None:
             api.copy_blocks(c, self.step_pairs, stream)
-        if fused:
+        if shared and self.shared_blocks:
+            B = self.q.shape[0]
+            if not fused:
+                api.kv_append(c, self.k_new, self.v_new, self.tables, self.ctx, stream)
+            api.decode_shared_prefix(c, self.q, self.tables, self.ctx, self.max_ctx, self.sm_scale, [0, B],
+                                     [self.shared_blocks], self.k_new if fused else None,
+                                     self.v_new if fused else None, self.out, self.shared_workspace, stream)
+        elif fused:
             api.decode_step(c, self.q, self.k_new, self.v_new, self.tables, self.ctx, self.max_ctx, self.sm_scale,
                             self.out, self.workspace, stream)
         else:

@@ -289,3 +289,39 @@ def test_prefix_cache_argument_checks():
     with pytest.raises(_lib.PagedAttnError):
         a.allocate_cached(1, [1])  # the id is taken
     assert L.pa_prefix_cache_size(None) == -1
+
+
+def _shared(c, gs, gb, **kw):
+    a = dict(q=0x3000, out=0x4000, act=_lib.PA_F16, hq=4, tables=0x5000, ctx=0x6000, B=3, mb=8, mctx=128,
+             scale=0.1, ws=0x7000, wsb=1 << 20)
+    a.update(kw)
+    gsa = (ctypes.c_int32 * len(gs))(*gs) if gs is not None else None
+    gba = (ctypes.c_int32 * len(gb))(*gb) if gb is not None else None
+    n = len(gb) if gb is not None else kw.get("ng", 0)
+    return _lib.lib().pa_decode_shared_prefix(ctypes.byref(c), a["q"], None, None, a["out"], a["act"], a["hq"],
+                                              a["tables"], a["ctx"], a["B"], a["mb"], a["mctx"], a["scale"], n, gsa,
+                                              gba, a["ws"], a["wsb"], None)
+
+
+def test_shared_prefix_argument_checks_fail_before_any_launch():
+    L = _lib.lib()
+    c = _cache()  # 16-token blocks, f16 pool
+    # groups must be ordered, inside the batch, and claim at most max_blocks / max_context_len
+    assert _shared(c, [0, 4], [2], B=0) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert _shared(c, [2, 1], [2], B=0) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert _shared(c, [-1, 1], [2], B=0) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert _shared(c, [0, 2], [9], B=0) == _lib.PA_ERR_INVALID_ARGUMENT      # 9 blocks > max_blocks 8
+    assert _shared(c, [0, 2], [-1], B=0) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert _shared(c, [0, 2], [8], mctx=100, B=0) == _lib.PA_ERR_INVALID_ARGUMENT  # 128 tokens > 100
+    assert _shared(c, None, None, ng=1, B=0) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert _shared(c, list(range(18)), [1] * 17, B=0) == _lib.PA_ERR_UNSUPPORTED   # more than 16 groups
+    assert _shared(c, [0, 2], [2], act=_lib.PA_F32) == _lib.PA_ERR_UNSUPPORTED
+    assert _shared(_cache(kv_dtype=_lib.PA_F32), [0, 2], [2], act=_lib.PA_F32) == _lib.PA_ERR_UNSUPPORTED
+    assert _shared(c, [0, 0, 0], [2, 1], B=0) == _lib.PA_OK
+    # workspace: prefix partials (256 tokens each) plus the decode's (512 each)
+    need = L.pa_decode_shared_workspace_size(3, 4, 128, 1000, 300)
+    assert need == 256 + 3 * 4 * (2 + 2) * (128 + 2) * 4
+    assert L.pa_decode_shared_workspace_size(3, 4, 128, 1000, 0) == L.pa_decode_workspace_size(3, 4, 128, 1000)
+    assert _shared(c, [0, 3], [19], mctx=1000, mb=64, wsb=need - 1) == _lib.PA_ERR_WORKSPACE_TOO_SMALL  # 304 tokens
+    # no group shares anything: the plain decode's rules (f32 allowed)
+    assert _shared(_cache(kv_dtype=_lib.PA_F32), [0, 0], [0], act=_lib.PA_F32, B=0) == _lib.PA_OK

@@ -1,0 +1,115 @@
+"""Shared-prefix decode (pa_decode_shared_prefix) against the CPU reference
+(needs an MI355X).
+
+Sequences that fork one prompt hold its full blocks in common [F55 §常见问题];
+[IPX §同一提示生成两个回答的假想例子].  The shared-prefix path reads those
+blocks once per KV head for all of a group's query rows, then each sequence's
+own tokens, and merges both; the output must be the same attention as over
+each whole context.  Cases cover FP8 and f16 pools, MHA, GQA and MQA, head
+sizes 32 to 128, block sizes 1 to 16, prefixes that end on and inside a block
+(the partial block is each sequence's own copy after copy-on-write), fused
+and separate append, several groups, sequences outside every group, and a
+group whose claim does not hold.
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_375_amd import api
+from paged_kv_cache_375_amd.workloads import WORKLOADS, Workload
+from tests.gpu_helpers import TOL, build_pair, out_f64, pool_bytes
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    Workload("sp_fp8_mha", 40, 40, 128, 16, 6, 1, 900, kv="e4m3", prefix_len=512),
+    Workload("sp_fp8_mha_505", 40, 40, 128, 16, 6, 1, 900, kv="e4m3", prefix_len=505),
+    Workload("sp_f16_gqa", 64, 8, 128, 16, 4, 1, 700, prefix_len=700),
+    Workload("sp_f16_mqa", 71, 1, 64, 16, 4, 1, 600, prefix_len=300),
+    Workload("sp_f16_mha_bs4", 8, 8, 64, 4, 5, 1, 800, prefix_len=257),
+    Workload("sp_fp8_gqa_d32_bs1", 12, 3, 32, 1, 5, 1, 400, kv="e4m3", prefix_len=130),
+]
+
+
+def _shared_blocks(wl):
+    return wl.prefix_len // wl.block_size
+
+
+def _run(gpu, group_start, group_blocks, fused):
+    if gpu.step_pairs is not None:
+        api.copy_blocks(gpu.cache, gpu.step_pairs)
+    if fused:
+        return api.decode_shared_prefix(gpu.cache, gpu.q, gpu.tables, gpu.ctx, gpu.max_ctx, gpu.sm_scale,
+                                        group_start, group_blocks, k_new=gpu.k_new, v_new=gpu.v_new)
+    api.kv_append(gpu.cache, gpu.k_new, gpu.v_new, gpu.tables, gpu.ctx)
+    return api.decode_shared_prefix(gpu.cache, gpu.q, gpu.tables, gpu.ctx, gpu.max_ctx, gpu.sm_scale,
+                                    group_start, group_blocks)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["with_append", "after_append"])
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_shared_prefix_parity(wl, fused):
+    print(f"[shared-prefix] {wl} fused={fused}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    shared = _shared_blocks(wl)
+    t = gpu.scenario.tables
+    assert (t[:, :shared] == t[0, :shared]).all()  # the sharing the call relies on
+    out = out_f64(_run(gpu, [0, wl.batch], [shared], fused))
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    err = float(np.max(np.abs(out - ref.decode())))
+    print(f"[shared-prefix] {wl.name}: max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]
+    again = out_f64(_run(gpu, [0, wl.batch], [shared], fused))
+    assert np.array_equal(out, again)  # deterministic; counters left at zero
+
+
+def test_shared_prefix_groups_and_outsiders():
+    """Groups [0, 2) sharing all 32 prefix blocks, an empty group, [2, 5)
+    claiming only 20 of them; sequences 5 and 6 decode as usual."""
+    wl = Workload("sp_groups", 40, 40, 128, 16, 7, 1, 700, kv="e4m3", prefix_len=512)
+    dr, gpu, ref = build_pair(wl)
+    out = out_f64(_run(gpu, [0, 2, 2, 5], [32, 7, 20], True))
+    ref.append()
+    err = float(np.max(np.abs(out - ref.decode())))
+    print(f"[shared-prefix] groups: max abs err {err:.3e}", flush=True)
+    assert err <= TOL["e4m3"]
+
+
+def test_shared_prefix_claim_past_a_context_gives_nan_for_that_sequence_only():
+    wl = Workload("sp_claim", 8, 8, 64, 16, 4, 1, 200, prefix_len=64)
+    dr, gpu, ref = build_pair(wl)
+    short = int(np.argmin(dr.ctx))
+    claim = (int(dr.ctx[short]) + 15) // 16  # covers the new token's slot: not a shared range
+    order = [short] + [s for s in range(wl.batch) if s != short]
+    perm = torch.tensor(order).cuda()
+    gpu.q, gpu.k_new, gpu.v_new = gpu.q[perm].contiguous(), gpu.k_new[perm].contiguous(), gpu.v_new[perm].contiguous()
+    gpu.tables, gpu.ctx = gpu.tables[perm].contiguous(), gpu.ctx[perm].contiguous()
+    out = out_f64(_run(gpu, [0, 1], [claim], True))
+    ref.append()
+    want = ref.decode()[order]
+    assert np.isnan(out[0]).all()
+    assert float(np.max(np.abs(out[1:] - want[1:]))) <= TOL["f16"]
+
+
+def test_full_prefix_workload_sampled_parity():
+    """The FP8 prefix workload at its real size, in the launch the benchmark
+    times for it (shared prefix, append fused)."""
+    wl = WORKLOADS["opt13b_fp8_prefix"]
+    print(f"[shared-prefix] {wl.name}: building", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    out = out_f64(_run(gpu, [0, wl.batch], [_shared_blocks(wl)], True))
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    rng = np.random.default_rng(12)
+    B, hq = wl.batch, wl.num_q_heads
+    longest, shortest = int(np.argmax(dr.ctx)), int(np.argmin(dr.ctx))
+    seqs = [longest] * hq + [shortest] * hq + rng.integers(0, B, 64).tolist()
+    heads = list(range(hq)) * 2 + rng.integers(0, hq, 64).tolist()
+    err = float(np.max(np.abs(out[np.array(seqs), np.array(heads)] - ref.decode_pairs(seqs, heads))))
+    print(f"[shared-prefix] {wl.name}: {len(seqs)} sampled outputs, max abs err {err:.3e}", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL["e4m3"]
