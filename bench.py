@@ -39,12 +39,17 @@ def workload_label(wl):
             + (f" after a shared {wl.prefix_len}-token prefix" if wl.prefix_len else ""))
 
 
-def decode_kernel_name(wl):
+def decode_kernel_name(wl, shared=False):
     """The decode kernel that serves the workload (matrix cores when query
-    heads share KV heads and activations are f16, else the per-head kernel)."""
+    heads share KV heads and activations are f16, else the per-head kernel),
+    after the prefix pass when a shared prefix takes the shared-prefix path."""
     if wl.num_q_heads > wl.num_kv_heads and wl.act == "f16":
-        return "decode_group_kernel (grouped heads on MFMA: append + split-context attention + merge)"
-    return "decode_kernel (per head on VALU: append + split-context attention + merge)"
+        k = "decode_group_kernel (grouped heads on MFMA: append + split-context attention + merge)"
+    else:
+        k = "decode_kernel (per head on VALU: append + split-context attention + merge)"
+    if shared:
+        k = "prefix pass (decode_group_kernel: the shared blocks once per KV head for every sequence, MFMA) + " + k
+    return k
 
 
 def kernel_source_hash():
@@ -203,6 +208,8 @@ def main():
     ap.add_argument("--writers", action="store_true",
                     help="instead of the decode step, time the pool writers (prompt write, append, block copy) "
                          "and print one JSON line per writer")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="decode a prefix workload with pa_decode_step like any other, not the shared-prefix path")
     ap.add_argument("--swap", action="store_true",
                     help="instead of the decode step, time block swaps to pinned host memory and back for each "
                          "block size (the workload's heads, head_dim and pool dtype)")
@@ -252,8 +259,9 @@ def main():
                              for _ in range(rotate - 1)]
     torch.cuda.synchronize()
 
+    shared = bool(step.shared_blocks) and not args.no_shared
     for i in range(args.warmup):
-        step.run(caches[i % rotate])
+        step.run(caches[i % rotate], shared=shared)
     torch.cuda.synchronize()
 
     api.timing_enable(True)
@@ -270,7 +278,7 @@ def main():
     for smp in range(n_samples):
         n = per if smp < n_samples - 1 else K - per * (n_samples - 1)
         for _ in range(n):
-            step.run(caches[i % rotate])
+            step.run(caches[i % rotate], shared=shared)
             i += 1
         evs[smp + 1].record(stream)
     torch.cuda.synchronize()
@@ -315,6 +323,8 @@ def main():
             "head_dim": wl.head_dim, "block_size": wl.block_size, "sum_ctx": int(sc.ctx.sum()),
             "max_ctx": int(sc.ctx.max()), "cow_pairs": int(len(sc.step_pairs)), "seed": args.seed,
             "layers": 1, "pool_bytes": pool_bytes, "pool_copies_rotated": rotate,
+            "path": "pa_decode_shared_prefix" if shared else "pa_decode_step",
+            "shared_prefix_blocks": step.shared_blocks if shared else 0,
         },
         "step_bytes": {"total": sb.total, "kv_read": sb.kv_read, "kv_read_unique": sb.kv_read_unique,
                        "append": sb.append, "q_out": sb.q_out, "tables": sb.tables, "cow": sb.cow},
@@ -326,7 +336,7 @@ def main():
                                 "max": max(sample_ms), "n": n_samples},
         "kernels_ms": {"decode_avg": part_avg_ms, "decode_launches": n_part},
         "wall_s_timed_region": wall,
-        "roofline": {"bound": "hbm", "kernel": decode_kernel_name(wl),
+        "roofline": {"bound": "hbm", "kernel": decode_kernel_name(wl, shared),
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},

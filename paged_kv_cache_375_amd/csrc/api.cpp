@@ -284,12 +284,18 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
   }
   hipError_t e = hipSuccess;
   if (a.ngroups > 0) {
-    // the prefix pass first (the timing brackets both launches)
+    // The prefix pass first, then the decode launch, on the caller's stream:
+    // the decode's first partition of each head starts from the prefix's
+    // partials.  (A prefix pass beside the decode on a second stream, the two
+    // meeting at per-row arrival counters, was slower: its workgroups waited
+    // for slots the decode's kept refilling.)  The timing events bracket both.
     if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
     a.ev[0] = nullptr;
     e = pa::launch_prefix_pass(a);
+    if (e == hipSuccess) e = pa::launch_decode(a);
+  } else {
+    e = pa::launch_decode(a);
   }
-  if (e == hipSuccess) e = pa::launch_decode(a);
   if (e == hipErrorInvalidValue) return fail(PA_ERR_UNSUPPORTED, "%s: unsupported dtype/shape combination", fn);
   if (timed && e == hipSuccess) g_timing.n_part += 1;
   return hip_status(e, fn);

@@ -171,7 +171,8 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
 }
 
 // BIG: block_size >= TPL (block id wave-uniform, table slice in registers).
-template <typename KV, typename ACT, int D, int NW, int U, bool BIG>
+// PRE: the launch follows a prefix pass (shared-prefix decode).
+template <typename KV, typename ACT, int D, int NW, int U, bool BIG, bool PRE>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   using M = Math<KV, ACT>;
   constexpr int EPL = M::EPL;
@@ -275,9 +276,28 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  // a shared prefix's partials enter through one row of lanes of partition 0
-  if (p == 0 && pf.pre > 0 && !bad_early && w == 0 && row == 0)
-    load_prefix_state<D, EPL>(P, sh, pf.pre, c * EPL, m, l, acc);
+  // A shared prefix: the prefix pass left pf.pre partials of this head
+  // (without the V scale), which partition 0 adds in its final combine.  Up
+  // to KPRE of them are loaded here, thread i taking element i, so they
+  // arrive while the partition streams its own tokens; more are read at the
+  // combine.
+  constexpr int KPRE = 4;
+  static_assert(NW * 64 >= D, "one combine element per thread");
+  const bool with_pre = PRE && p == 0 && pf.pre > 0;
+  float pre_m[KPRE], pre_l[KPRE], pre_o[KPRE];
+  if constexpr (PRE) {
+    if (with_pre && pf.pre <= KPRE && tid < D) {
+#pragma unroll
+      for (int q = 0; q < KPRE; ++q) {
+        if (q < pf.pre) {
+          const float* ml = P.ws_ml + (sh * P.max_parts + q) * 2;
+          pre_m[q] = coherent_load(ml);
+          pre_l[q] = coherent_load(ml + 1);
+          pre_o[q] = coherent_load(P.ws_o + (sh * P.max_parts + q) * D + tid);
+        }
+      }
+    }
+  }
 
   const int nrounds = bad_early ? 0 : (t1 - t0 + ROUND - 1) / ROUND;
   for (int r0 = 0; r0 < nrounds; r0 += U) {
@@ -364,6 +384,20 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
     float mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < NW; ++v) mx = fmaxf(mx, red_m[v]);
+    // the prefix partials' (m, l, o), from registers or read now
+    auto pm = [&](int q) {
+      return q < KPRE && pf.pre <= KPRE ? pre_m[q] : coherent_load(P.ws_ml + (sh * P.max_parts + q) * 2);
+    };
+    auto pl = [&](int q) {
+      return q < KPRE && pf.pre <= KPRE ? pre_l[q] : coherent_load(P.ws_ml + (sh * P.max_parts + q) * 2 + 1);
+    };
+    auto po = [&](int q) {
+      return q < KPRE && pf.pre <= KPRE ? pre_o[q] : coherent_load(P.ws_o + (sh * P.max_parts + q) * D + i);
+    };
+    if constexpr (PRE) {
+      if (with_pre)
+        for (int q = 0; q < pf.pre; ++q) mx = fmaxf(mx, pm(q));
+    }
     const float mu = (mx == -INFINITY) ? 0.f : mx;
     float o = 0.f, L = 0.f;
 #pragma unroll
@@ -371,6 +405,15 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
       const float f = exp2f(red_m[v] - mu);
       o += f * red_o[v][i];
       L += f * red_l[v];
+    }
+    if constexpr (PRE) {
+      if (with_pre) {
+        for (int q = 0; q < pf.pre; ++q) {
+          const float f = exp2f(pm(q) - mu);
+          o += f * po(q);
+          L += f * pl(q);
+        }
+      }
     }
     if (bad_early) o = L = mx = NAN;
     if (nparts == 1) {
@@ -411,7 +454,11 @@ hipError_t decode_t(const DecodeArgs& a) {
   const DecodeParams P = make_decode_params(a);
   const unsigned np = static_cast<unsigned>(decode_grid_parts(a, kPartitionTokens));
   const dim3 grid(PA_GRID_HEAD_FIRST ? a.num_q_heads : np, PA_GRID_HEAD_FIRST ? np : a.num_q_heads, a.num_seqs);
-  auto kern = c.block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true> : decode_kernel<KV, ACT, D, NW, U, false>;
+  auto kern = a.ngroups > 0
+                  ? (c.block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true, true>
+                                         : decode_kernel<KV, ACT, D, NW, U, false, true>)
+                  : (c.block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true, false>
+                                         : decode_kernel<KV, ACT, D, NW, U, false, false>);
   if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, a.stream, P);
   const hipError_t e = hipGetLastError();
