@@ -125,16 +125,50 @@ struct Math<float, float> {  // f32 pool, f32 query
   }
 };
 
-template <typename ACT>
-struct Math<fp8_t, ACT> {  // E4M3 pool: exact hardware conversion to f32
+template <>
+struct Math<fp8_t, half_t> {  // E4M3 pool, f16 query: K converted to f16 pairs (exact) for packed dots
+  static constexpr int EPL = 16;
+  struct Q {
+    uint32_t w[8];  // the 16 query values as f16 pairs
+  };
+  static __device__ __forceinline__ Q load_q(const half_t* q) {
+    const Vec16 a = load16(q), b = load16(q + 8);
+    return Q{{a.w[0], a.w[1], a.w[2], a.w[3], b.w[0], b.w[1], b.w[2], b.w[3]}};
+  }
+  static __device__ __forceinline__ float dot(const Vec16& k, const Q& q) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // bytes 0, 1 and 2, 3 of the word: elements 4i, 4i + 1 and 4i + 2, 4i + 3
+      const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.w[i], 1.0f, false);
+      const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.w[i], 1.0f, true);
+      acc = __builtin_amdgcn_fdot2(lo, __builtin_bit_cast(half2_t, q.w[2 * i]), acc, false);
+      acc = __builtin_amdgcn_fdot2(hi, __builtin_bit_cast(half2_t, q.w[2 * i + 1]), acc, false);
+    }
+    return acc;
+  }
+  static __device__ __forceinline__ void axpy(float* acc, const Vec16& v, float p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float2_t lo = e4m3x2_to_f32(v.w[i], false), hi = e4m3x2_to_f32(v.w[i], true);
+      acc[4 * i] += p * lo[0];
+      acc[4 * i + 1] += p * lo[1];
+      acc[4 * i + 2] += p * hi[0];
+      acc[4 * i + 3] += p * hi[1];
+    }
+  }
+};
+
+template <>
+struct Math<fp8_t, float> {  // E4M3 pool, f32 query: exact hardware conversion to f32
   static constexpr int EPL = 16;
   struct Q {
     float f[16];
   };
-  static __device__ __forceinline__ Q load_q(const ACT* q) {
+  static __device__ __forceinline__ Q load_q(const float* q) {
     Q r;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) r.f[i] = to_f32(q[i]);
+    for (int i = 0; i < 16; ++i) r.f[i] = q[i];
     return r;
   }
   static __device__ __forceinline__ float dot(const Vec16& k, const Q& q) {
