@@ -245,6 +245,9 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   const int64_t head_rows = static_cast<int64_t>(g) * bs;      // token rows before head g in a block
   const int64_t block_rows = static_cast<int64_t>(P.hkv) * bs;  // token rows per block
 
+  // q is loaded first, so its latency overlaps the table slice's
+  const typename M::Q qr = M::load_q(static_cast<const ACT*>(P.q) + sh * D + c * EPL);
+
   __shared__ int tab[BIG ? 1 : PART];
   __shared__ float red_m[NW], red_l[NW];
   __shared__ float red_o[NW][D];
@@ -304,8 +307,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
     }
   }
   const bool bad_early = __syncthreads_or(my_bad) != 0;
-
-  const typename M::Q qr = M::load_q(static_cast<const ACT*>(P.q) + sh * D + c * EPL);
   float m = -INFINITY, l = 0.f;
   float acc[EPL];
 #pragma unroll

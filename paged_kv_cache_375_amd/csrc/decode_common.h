@@ -104,6 +104,35 @@ __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16- and 8-byte device-coherent accesses to a window [base, base + bytes)
+// of float data through a buffer resource.  The resource sits in scalar
+// registers, so `base` must be the same for the whole wave; lanes pass byte
+// offsets.  The accesses carry the cache policy of the 4-byte ones above
+// (SC1: stores written through to memory, loads served from past this XCD's
+// L2).  The hardware range check reads zeros for, and drops stores to,
+// offsets at or past `bytes`.
+struct CoherentWindow {
+  static constexpr int kSc1 = 16;            // cache-policy operand: SC1
+  static constexpr int kWord3 = 0x00020000;  // 32-bit data format, untyped access
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ CoherentWindow(const float* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, static_cast<int>(bytes), kWord3)) {}
+  __device__ __forceinline__ float4_t load4(uint32_t off) const {
+    return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+  }
+  __device__ __forceinline__ float2_t load2(uint32_t off) const {
+    return __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSc1));
+  }
+  __device__ __forceinline__ void store4(uint32_t off, float4_t v) const {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kSc1);
+  }
+  __device__ __forceinline__ void store2(uint32_t off, float2_t v) const {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, kSc1);
+  }
+};
+
 // The new token's 16-byte chunk c in pool format (quantised for FP8 pools),
 // read from a [head_dim] row of activations.
 template <typename KV, typename ACT>
@@ -187,23 +216,44 @@ constexpr int kMergeCap = kMaxPartitions;
 // left (m_p, l_p) (running max in log2 units and weight sum) and the
 // unnormalised vector o_p; the result is
 //   out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p,
-// the same rescaling the online softmax does within a partition.  All loads
-// of a stage are independent (partials are read with device-coherent loads:
-// other workgroups wrote them, possibly on another XCD).  mw, ww: LDS
-// scratch of kMergeCap floats each.  NT threads take part; the caller
-// synchronises before the call.
-template <typename ACT, int D, int NT>
+// the same rescaling the online softmax does within a partition.  Partials
+// are read with device-coherent loads (other workgroups wrote them,
+// possibly on another XCD), 8 or 16 bytes at a time; each thread issues
+// the loads of up to U output items before it uses any, so one memory
+// latency serves them all.  The sum over partitions runs in partition
+// order whatever U is.  mw, ww: LDS scratch of kMergeCap floats each.  NT
+// threads take part; the caller synchronises before the call.
+template <typename ACT, int D, int NT, int U = 1>
 __device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh0, int nh, int slot0, int nparts,
                                                int tid, float* mw, float* ww) {
+  static_assert(U >= 1 && U <= 4, "items in flight per thread");
   ACT* out = static_cast<ACT*>(P.out);
+  const int64_t stride = P.max_parts;  // slots per workspace row
+  // rows sh0 .. sh0 + nh - 1, slots slot0 .. slot0 + nparts - 1 (at most
+  // 80 rows x kMaxPartitions slots x 512 bytes: 32-bit offsets suffice)
+  const uint32_t span = static_cast<uint32_t>((nh - 1) * stride + nparts);
+  const CoherentWindow wml(P.ws_ml + (sh0 * stride + slot0) * 2, span * 8u);
+  const CoherentWindow wo(P.ws_o + (sh0 * stride + slot0) * D, span * (D * 4u));
   const int hb = max(1, min(nh, kMergeCap / nparts));  // heads per batch
   for (int hbase = 0; hbase < nh; hbase += hb) {
     const int nb = min(hb, nh - hbase);
-    for (int i = tid; i < nb * nparts; i += NT) {
-      const int hh = i / nparts, q = i - hh * nparts;
-      const float* ml = P.ws_ml + ((sh0 + hbase + hh) * P.max_parts + slot0 + q) * 2;
-      mw[i] = coherent_load(ml);
-      ww[i] = coherent_load(ml + 1);
+    const int pairs = nb * nparts;
+    for (int i0 = tid; i0 < pairs; i0 += 2 * NT) {
+      float2_t x[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = min(i0 + u * NT, pairs - 1);  // past the end: re-read the last pair
+        const int hh = i / nparts, q = i - hh * nparts;
+        x[u] = wml.load2(static_cast<uint32_t>((hbase + hh) * stride + q) * 8u);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * NT;
+        if (i < pairs) {
+          mw[i] = x[u][0];
+          ww[i] = x[u][1];
+        }
+      }
     }
     __syncthreads();
     for (int hh = tid; hh < nb; hh += NT) {
@@ -219,34 +269,55 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh
       for (int q = 0; q < nparts; ++q) ww[hh * nparts + q] = mw[hh * nparts + q] * inv;
     }
     __syncthreads();
-    // four consecutive output elements per thread; partials in groups of four
-    for (int i = tid; i < nb * (D / 4); i += NT) {
+    // four consecutive output elements per item
+    const int items = nb * (D / 4);
+    auto item_off = [&](int i, int q) -> uint32_t {
+      const int hh = i / (D / 4), d = (i - hh * (D / 4)) * 4;
+      return static_cast<uint32_t>(((hbase + hh) * stride + q) * D + d) * 4u;
+    };
+    auto finish = [&](int i, const float4_t& acc) {
       const int hh = i / (D / 4), d = (i - hh * (D / 4)) * 4;
       const int64_t sh = sh0 + hbase + hh;
-      const float* o = P.ws_o + (sh * P.max_parts + slot0) * D + d;
-      const float* w = ww + hh * nparts;
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      int q = 0;
-      for (; q + 4 <= nparts; q += 4) {
-        float x[4][4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[u][e] = coherent_load(o + (q + u) * D + e);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] += w[q + u] * x[u][e];
-      }
-      for (; q < nparts; ++q) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = coherent_load(o + q * D + e);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += w[q] * x[e];
-      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[sh * D + d + e] = from_f32<ACT>(acc[e]);
+    };
+    if (nparts <= 4) {
+      for (int i0 = tid; i0 < items; i0 += U * NT) {
+        float4_t x[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = min(i0 + u * NT, items - 1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q < nparts) x[u][q] = wo.load4(item_off(i, q));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * NT;
+          if (i >= items) continue;
+          const float* w = ww + (i / (D / 4)) * nparts;
+          float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (q < nparts) acc += w[q] * x[u][q];
+          finish(i, acc);
+        }
+      }
+    } else {
+      for (int i = tid; i < items; i += NT) {
+        const float* w = ww + (i / (D / 4)) * nparts;
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        int q = 0;
+        for (; q + 4 <= nparts; q += 4) {
+          float4_t x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) x[u] = wo.load4(item_off(i, q + u));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc += w[q + u] * x[u];
+        }
+        for (; q < nparts; ++q) acc += w[q] * wo.load4(item_off(i, q));
+        finish(i, acc);
+      }
     }
     __syncthreads();
   }

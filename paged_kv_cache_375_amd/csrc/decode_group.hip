@@ -58,7 +58,6 @@ constexpr int group_occupancy() {
 }
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 32;  // tokens per chunk: two 16-row tiles of the first product
 constexpr float kLazy = 8.f;  // running-max slack, log2 units (weights <= 256)
@@ -130,7 +129,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   using L = Layout<KV, D>;
   constexpr int KVB = L::KVB, NS = L::NS, NDT = L::NDT, NV = L::NV, LCH = L::LCH;
   constexpr int VCH = L::VCH;
-  constexpr int MREGS = HT * NDT * 4 + 2 * HT;  // floats per lane in a wave's partial result
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,8 +160,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   } else {
     grp = blockIdx.x % groups_per_kv;
     kvh = blockIdx.x / groups_per_kv;
-    p = blockIdx.y;
-    s = blockIdx.z;
+    s = blockIdx.y;
+    p = blockIdx.z;
     ctx = P.ctx[s];
     // tokens [0, begin) of a shared prefix were covered by the prefix pass
     pf = seq_prefix(P, s);
@@ -197,7 +195,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   // each wave's K, then V, chunk as f16 rows; afterwards the merge's scratch
   constexpr int kVbuf = NW * kChunk * LCH > kMergeCap / 2 ? NW * kChunk * LCH : kMergeCap / 2;
   __shared__ uint4 vbuf[kVbuf];
-  __shared__ float mbuf[MREGS][64];         // one wave's partial result, for the merge
+  // one wave's partial result, for the merge: 16 and 8 bytes per lane
+  __shared__ float4_t mbo[HT * NDT][64];
+  __shared__ float2_t mbl[HT][64];
   __shared__ int is_last;
   __shared__ Vec16 newkv[2][VCH];  // the new token's K and V rows in pool format
   __shared__ uint4 qs[HT * 16 * LCH];  // the workgroup's q rows (f16), zero past the group
@@ -219,11 +219,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   // from the caller's rows instead of the pool.
   const bool has_new = !PREFIX && P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
   if (has_new && grp == 0 && w == 0) store_new_token<KV, half_t, D>(P, s, kvh, ctx, lane);
-  for (int i = tid; i < HT * 16 * LCH; i += NW * 64) {
-    const int hh = i / LCH, ch = i % LCH;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (hh < nh) x = *reinterpret_cast<const uint4*>(static_cast<const half_t*>(P.q) + row_sh(hh) * D + ch * 8);
-    qs[hh * LCH + (ch ^ L::swz_k(hh))] = x;
+  // Scores stay unscaled until the exponent.  A negative scale is folded
+  // into q (negation is exact), so the scale applied there, |score_scale|,
+  // keeps the order of the scores.
+  const bool qneg = P.score_scale < 0.f;
+  const float sscale = fabsf(P.score_scale);
+  {
+    // every q load of a thread is issued before the first LDS store
+    constexpr int QN = (HT * 16 * LCH + NW * 64 - 1) / (NW * 64);
+    uint4 x[QN];
+#pragma unroll
+    for (int k = 0; k < QN; ++k) {
+      const int i = tid + k * NW * 64, hh = i / LCH, ch = i % LCH;
+      x[k] = make_uint4(0, 0, 0, 0);
+      if (i < HT * 16 * LCH && hh < nh)
+        x[k] = *reinterpret_cast<const uint4*>(static_cast<const half_t*>(P.q) + row_sh(hh) * D + ch * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < QN; ++k) {
+      const int i = tid + k * NW * 64, hh = i / LCH, ch = i % LCH;
+      if (qneg) x[k] = make_uint4(x[k].x ^ 0x80008000u, x[k].y ^ 0x80008000u, x[k].z ^ 0x80008000u, x[k].w ^ 0x80008000u);
+      if (i < HT * 16 * LCH) qs[hh * LCH + (ch ^ L::swz_k(hh))] = x[k];
+    }
   }
   if (has_new && tid < 2 * VCH) {
     const int64_t src = (static_cast<int64_t>(s) * P.hkv + kvh) * D * static_cast<int64_t>(sizeof(half_t));
@@ -363,7 +380,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
     rows_to_lds(kr, L::swz_k);
     if (nx < nchunks) load_rows(kr, P.kc, nx);
 
-    // scores S^T: lane (g, n) gets tokens 16 tau + 4 g + i of head 16 ht + n
+    // scores S^T (unscaled): lane (g, n) gets tokens 16 tau + 4 g + i of
+    // head 16 ht + n
+    const bool last = cb + kChunk > t1;  // the partition's last chunk: tokens past its end are masked
     float sc[HT][8];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
@@ -377,8 +396,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
 #pragma unroll
         for (int st = 0; st < NS; ++st) acc = mfma16x16x32(ka[st], q_operand(ht, st), acc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[ht][4 * tau + i] = acc[i] * P.score_scale;
-        if (cb + kChunk > t1) {  // the partition's last chunk: mask tokens past its end
+        for (int i = 0; i < 4; ++i) sc[ht][4 * tau + i] = acc[i];
+        if (last) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (cb + 16 * tau + 4 * g + i >= t1) sc[ht][4 * tau + i] = -INFINITY;
@@ -393,7 +412,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
     // online softmax per head column; the weights become the B operand.
     // The running max moves only when a chunk's max exceeds it by more than
     // kLazy (log2 units), so weights stay at most 2^kLazy and the rescale of
-    // the accumulators is skipped by the whole wave in most chunks.
+    // the accumulators is skipped by the whole wave in most chunks.  The
+    // chunk's max is taken over unscaled scores and then scaled (rounding
+    // is monotonic and sscale >= 0); each weight is 2^(score * sscale - m)
+    // with one rounding.
     half8_t pf[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -402,6 +424,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
       for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[ht][j]);
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      mloc *= sscale;
       const bool raise = mloc > m[ht] + kLazy;  // uniform within a head column
       if (__any(raise)) {
         const float m_new = raise ? mloc : m[ht];
@@ -411,13 +434,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
         for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= alpha;
         m[ht] = m_new;
       }
+      // weights as f16 pairs; their sum is taken from those same f16 values
+      // (a dot product with ones: exact products, f32 accumulation)
+      half2_t hp[4];
       float psum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const _Float16 ph = static_cast<_Float16>(fast_exp2(sc[ht][j] - m[ht]));
-        pf[ht][j] = ph;
-        psum += static_cast<float>(ph);  // the weights the product uses
+      for (int k = 0; k < 4; ++k) {
+        const float2_t e = {fast_exp2(fmaf(sc[ht][2 * k], sscale, -m[ht])),
+                            fast_exp2(fmaf(sc[ht][2 * k + 1], sscale, -m[ht]))};
+        hp[k] = __builtin_convertvector(e, half2_t);
       }
+      if (last) {  // masked tokens weigh zero (also when sscale is 0)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (cb + 16 * (j >> 2) + 4 * g + (j & 3) >= t1) hp[j >> 1][j & 1] = 0;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) psum = __builtin_amdgcn_fdot2(hp[k], half2_t{1, 1}, psum, false);
+      pf[ht] = __builtin_bit_cast(half8_t, hp);
       lsum[ht] += psum;
     }
 
@@ -463,33 +497,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   // NW-2, ..., 1 into 0 (lane l merges with lane l; layouts are identical)
   for (int src = NW - 1; src >= 1; --src) {
     if (w == src) {
-      int k = 0;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        mbuf[k++][lane] = m[ht];
-        mbuf[k++][lane] = lsum[ht];
+        mbl[ht][lane] = float2_t{m[ht], lsum[ht]};
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mbuf[k++][lane] = o[ht][dt][i];
+        for (int dt = 0; dt < NDT; ++dt) mbo[ht * NDT + dt][lane] = o[ht][dt];
       }
     }
     __syncthreads();
     if (w == src - 1) {
-      int k = 0;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        const float mo = mbuf[k++][lane];
-        const float lo = mbuf[k++][lane];
+        const float2_t ml = mbl[ht][lane];
+        const float mo = ml[0], lo = ml[1];
         const float mn = fmaxf(m[ht], mo);
         const float mu = (mn == -INFINITY) ? 0.f : mn;
         const float a = exp2f(m[ht] - mu), b = exp2f(mo - mu);
         lsum[ht] = lsum[ht] * a + lo * b;
         m[ht] = mn;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int dt = 0; dt < NDT; ++dt) {
+          const float4_t y = mbo[ht * NDT + dt][lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[ht][dt][i] = o[ht][dt][i] * a + mbuf[k++][lane] * b;
+          for (int i = 0; i < 4; ++i) o[ht][dt][i] = o[ht][dt][i] * a + y[i] * b;
+        }
       }
     }
     __syncthreads();
@@ -501,6 +532,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   // prefix's
   const bool direct = !PREFIX && nparts == 1;
   const int slot = PREFIX ? p : pf.pre + p;
+  // decode rows are consecutive (s * hq + h0 + hh): windows from the first
+  const int64_t row0 = static_cast<int64_t>(s) * P.hq + h0;
+  const uint32_t rows_span = static_cast<uint32_t>((nh - 1) * static_cast<int64_t>(P.max_parts) + 1);
+  const CoherentWindow wso(P.ws_o + (row0 * P.max_parts + slot) * D, rows_span * (D * 4u));
+  const CoherentWindow wsml(P.ws_ml + (row0 * P.max_parts + slot) * 2, rows_span * 8u);
   if (w == 0) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
@@ -523,9 +559,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
           const float4_t nan4 = {NAN, NAN, NAN, NAN};
           *reinterpret_cast<float4_t*>(P.ws_o + (sh * P.max_parts + slot) * D + d) = bad ? nan4 : o[ht][dt];
         } else {
-          float* dst = P.ws_o + (sh * P.max_parts + slot) * D + d;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) coherent_store(dst + i, bad ? NAN : o[ht][dt][i] * P.v_scale);
+          const float4_t nan4 = {NAN, NAN, NAN, NAN};
+          wso.store4(static_cast<uint32_t>(hh * static_cast<int64_t>(P.max_parts) * D + d) * 4u,
+                     bad ? nan4 : o[ht][dt] * P.v_scale);
         }
       }
       if (!direct && g == 0) {
@@ -533,8 +569,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
           P.ws_ml[(sh * P.max_parts + slot) * 2] = mx;
           P.ws_ml[(sh * P.max_parts + slot) * 2 + 1] = lx;
         } else {
-          coherent_store(&P.ws_ml[(sh * P.max_parts + slot) * 2], mx);
-          coherent_store(&P.ws_ml[(sh * P.max_parts + slot) * 2 + 1], lx);
+          wsml.store2(static_cast<uint32_t>(hh * static_cast<int64_t>(P.max_parts)) * 8u, float2_t{mx, lx});
         }
       }
     }
@@ -553,8 +588,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   if (!is_last) return;
   // the V staging buffers are free now: they hold the merge's scratch
   float* scratch = reinterpret_cast<float*>(vbuf);
-  merge_partials<half_t, D, NW * 64>(P, static_cast<int64_t>(s) * P.hq + h0, nh, pf.pre, nparts, tid, scratch,
-                                     scratch + kMergeCap);
+  constexpr int kMergeItems = (HT * 16 * (D / 4) + NW * 64 - 1) / (NW * 64);
+  merge_partials<half_t, D, NW * 64, (kMergeItems < 4 ? kMergeItems : 4)>(
+      P, static_cast<int64_t>(s) * P.hq + h0, nh, pf.pre, nparts, tid, scratch, scratch + kMergeCap);
   if (tid == 0) __hip_atomic_store(&P.counters[cidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -591,8 +627,13 @@ hipError_t launch_ht(const DecodeArgs& a, int groups) {
   DecodeParams P = make_decode_params(a);
   P.part_tokens = part;
   const int grid_parts = decode_grid_parts(a, part);
-  const dim3 grid(static_cast<unsigned>(a.cache->num_kv_heads * groups), static_cast<unsigned>(grid_parts),
-                  static_cast<unsigned>(a.num_seqs));
+  // Dispatch order runs over (KV head, group), then sequences, then
+  // partitions: consecutive workgroups go to different XCDs, so every
+  // partition index (the first ones are the longest and the only ones
+  // every sequence has) spreads evenly over the XCDs, and workgroups past a
+  // sequence's last partition come last.
+  const dim3 grid(static_cast<unsigned>(a.cache->num_kv_heads * groups), static_cast<unsigned>(a.num_seqs),
+                  static_cast<unsigned>(grid_parts));
   if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, a.stream, P, groups);
   const hipError_t e = hipGetLastError();
