@@ -138,3 +138,23 @@ def test_full_workload_sampled_parity(name):
     print(f"[full] {name}: {len(seqs)} sampled outputs, max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
     assert np.all(np.isfinite(out))
     assert err <= TOL[wl.kv]
+
+
+@pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.35], ids=["negative", "zero", "large"])
+@pytest.mark.parametrize("case", [(71, 1, 64, "f16", 16), (64, 8, 128, "e4m3", 16), (16, 16, 128, "f16", 16)],
+                         ids=["mqa_grouped", "gqa_fp8_grouped", "mha_per_head"])
+def test_any_finite_scale(case, scale):
+    """The score scale may be any finite number.  The grouped kernel keeps
+    scores unscaled until the exponent and folds a negative scale into q; a
+    zero scale gives every token the same weight (the mean of V), masked
+    tokens still none; a large one makes the weights nearly one-hot."""
+    wl = _wl(*case)
+    print(f"[group] {wl} scale={scale}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    gpu.sm_scale = ref.sm_scale = float(np.float32(scale))
+    out = out_f64(gpu.run())
+    ref.append()
+    err = float(np.max(np.abs(out - ref.decode())))
+    print(f"[group] {wl.name} scale {scale}: max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]
