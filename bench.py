@@ -41,12 +41,13 @@ def workload_label(wl):
 
 def decode_kernel_name(wl, shared=False):
     """The decode kernel that serves the workload (matrix cores when query
-    heads share KV heads and activations are f16, else the per-head kernel),
-    after the prefix pass when a shared prefix takes the shared-prefix path."""
+    heads share KV heads and activations are f16, else the per-head kernel
+    and its merge launch), after the prefix pass when a shared prefix takes
+    the shared-prefix path."""
     if wl.num_q_heads > wl.num_kv_heads and wl.act == "f16":
         k = "decode_group_kernel (grouped heads on MFMA: append + split-context attention + merge)"
     else:
-        k = "decode_kernel (per head on VALU: append + split-context attention + merge)"
+        k = "decode_kernel (per head on VALU: append + split-context attention) + merge_kernel (split-context merge)"
     if shared:
         k = "prefix pass (decode_group_kernel: the shared blocks once per KV head for every sequence, MFMA) + " + k
     return k

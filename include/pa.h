@@ -181,10 +181,12 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  * multi-query attention share one KV head among contiguous query heads
  * [F55 §后来的做法]).  q, out: device [num_seqs][num_q_heads][head_dim] of
  * dtype act; fp32 accumulation; the output is rounded to act (nearest even).
- * Contexts longer than one 512-token partition are split; each partition's
- * (max, sum, vector) partial result is merged exactly, in the same launch,
- * by the last partition of that (sequence, head) to finish (the online
- * softmax gives the same result [F55 related plate F51]).
+ * Contexts longer than one 512-token partition are split; the partitions'
+ * (max, sum, vector) partial results are merged exactly (the online softmax
+ * gives the same result [F55 related plate F51]): by a second, small launch
+ * on the same stream for the per-head kernel (MHA, and f32 activations),
+ * and in the same launch, by the last partition of a (sequence, head group)
+ * to finish, for the grouped kernel (GQA/MQA with f16 activations).
  *
  * max_context_len must be >= every context_lens[s] and at most 524,288
  * (1024 partitions; larger values return PA_ERR_UNSUPPORTED); workspace must hold

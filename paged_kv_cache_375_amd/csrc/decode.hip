@@ -1,6 +1,6 @@
-// Paged decode attention in one launch: split-context partitions, an exact
-// merge by the last partition to finish, and optionally the append of the
-// step's new token.
+// Paged decode attention: split-context partitions and optionally the
+// append of the step's new token in one launch, then an exact merge of the
+// partitions' partial results by a small second launch (merge_kernel).
 //
 // One workgroup per (partition of kPartitionTokens tokens, query head,
 // sequence).  Every wavefront streams K/V rows with 16-byte loads: a token's
@@ -205,8 +205,11 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
 }
 
 // BIG: block_size >= TPL (block id wave-uniform, table slice in registers).
-// PRE: the launch follows a prefix pass (shared-prefix decode).
-template <typename KV, typename ACT, int D, int NW, int U, bool BIG, bool PRE>
+// A head whose tokens span several partitions, or whose sequence follows a
+// shared prefix (whose pass left partials in slots 0 .. pre - 1), leaves a
+// partial per partition in slot pre + p for merge_kernel; a head with a
+// single partial writes its output.
+template <typename KV, typename ACT, int D, int NW, int U, bool BIG>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   using M = Math<KV, ACT>;
   constexpr int EPL = M::EPL;
@@ -229,9 +232,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   // A shared prefix's tokens [0, begin) were covered by the prefix pass, which
   // left `pre` partials; the new token may not lie in them.
   const SeqPrefix pf = seq_prefix(P, s);
-  const bool bad_len = ctx < 0 || ctx > P.max_ctx ||
-                       static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) * bs || ctx < pf.begin ||
-                       (P.k_new != nullptr && pf.pre > 0 && ctx - 1 < pf.begin);
+  const bool bad_len = seq_bad_len(P, ctx, pf);
   // this launch's partitions; partition 0 starts from the prefix's merged
   // state, so these are all the partials to merge
   const int nparts = bad_len ? 1 : max(1, (ctx - pf.begin + PART - 1) / PART);
@@ -251,7 +252,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   __shared__ int tab[BIG ? 1 : PART];
   __shared__ float red_m[NW], red_l[NW];
   __shared__ float red_o[NW][D];
-  __shared__ int is_last;
   int my_bad = bad_len ? 1 : 0;
   // BIG: the partition's table slice lives in registers, entry i in lane
   // i % 64 of tabreg[i / 64]; a wave-uniform index is read with readlane.
@@ -311,28 +311,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  // A shared prefix: the prefix pass left pf.pre partials of this head
-  // (without the V scale), which partition 0 adds in its final combine.  Up
-  // to KPRE of them are loaded here, thread i taking element i, so they
-  // arrive while the partition streams its own tokens; more are read at the
-  // combine.
-  constexpr int KPRE = 4;
-  static_assert(NW * 64 >= D, "one combine element per thread");
-  const bool with_pre = PRE && p == 0 && pf.pre > 0;
-  float pre_m[KPRE], pre_l[KPRE], pre_o[KPRE];
-  if constexpr (PRE) {
-    if (with_pre && pf.pre <= KPRE && tid < D) {
-#pragma unroll
-      for (int q = 0; q < KPRE; ++q) {
-        if (q < pf.pre) {
-          const float* ml = P.ws_ml + (sh * P.max_parts + q) * 2;
-          pre_m[q] = coherent_load(ml);
-          pre_l[q] = coherent_load(ml + 1);
-          pre_o[q] = coherent_load(P.ws_o + (sh * P.max_parts + q) * D + tid);
-        }
-      }
-    }
-  }
 
   const int nrounds = bad_early ? 0 : (t1 - t0 + ROUND - 1) / ROUND;
   for (int r0 = 0; r0 < nrounds; r0 += U) {
@@ -419,20 +397,6 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
     float mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < NW; ++v) mx = fmaxf(mx, red_m[v]);
-    // the prefix partials' (m, l, o), from registers or read now
-    auto pm = [&](int q) {
-      return q < KPRE && pf.pre <= KPRE ? pre_m[q] : coherent_load(P.ws_ml + (sh * P.max_parts + q) * 2);
-    };
-    auto pl = [&](int q) {
-      return q < KPRE && pf.pre <= KPRE ? pre_l[q] : coherent_load(P.ws_ml + (sh * P.max_parts + q) * 2 + 1);
-    };
-    auto po = [&](int q) {
-      return q < KPRE && pf.pre <= KPRE ? pre_o[q] : coherent_load(P.ws_o + (sh * P.max_parts + q) * D + i);
-    };
-    if constexpr (PRE) {
-      if (with_pre)
-        for (int q = 0; q < pf.pre; ++q) mx = fmaxf(mx, pm(q));
-    }
     const float mu = (mx == -INFINITY) ? 0.f : mx;
     float o = 0.f, L = 0.f;
 #pragma unroll
@@ -441,44 +405,109 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
       o += f * red_o[v][i];
       L += f * red_l[v];
     }
-    if constexpr (PRE) {
-      if (with_pre) {
-        for (int q = 0; q < pf.pre; ++q) {
-          const float f = exp2f(pm(q) - mu);
-          o += f * po(q);
-          L += f * pl(q);
-        }
-      }
-    }
     if (bad_early) o = L = mx = NAN;
-    if (nparts == 1) {
+    // The output itself when this is the head's only partial, else a
+    // partial for merge_kernel.  Plain stores: the merge runs in the next
+    // launch, after this one's writes are visible device-wide.  Leaving the
+    // merge to a second launch frees each workgroup as soon as its partial
+    // is stored; merging in this launch (the last partition to finish, found
+    // with an arrival counter) held every split workgroup for the stores'
+    // completion and a counter round trip (OPT-13B layer 120.8 -> 117.2 us).
+    if (bad_len || pf.pre + nparts == 1) {
       out[sh * D + i] = from_f32<ACT>(bad_early ? NAN : (ctx > 0 ? o / L * P.v_scale : 0.f));
     } else {
       const int slot = pf.pre + p;
-      coherent_store(&P.ws_o[(sh * P.max_parts + slot) * D + i], o * P.v_scale);
+      P.ws_o[(sh * P.max_parts + slot) * D + i] = o * P.v_scale;
       if (i == 0) {
-        coherent_store(&P.ws_ml[(sh * P.max_parts + slot) * 2], mx);
-        coherent_store(&P.ws_ml[(sh * P.max_parts + slot) * 2 + 1], L);
+        P.ws_ml[(sh * P.max_parts + slot) * 2] = mx;
+        P.ws_ml[(sh * P.max_parts + slot) * 2 + 1] = L;
       }
     }
   }
-  if (nparts == 1) return;
+}
 
-  // Split context: the last partition to finish merges all partials of this
-  // (sequence, head) exactly and restores the arrival counter to zero.
-  // Partials are written and read with device-coherent accesses (they bypass
-  // the per-XCD L2, which other XCDs do not see), and every store has
-  // completed (s_waitcnt) before the counter is bumped, so the last arrival
-  // reads every partial without a whole-L2 write-back or invalidate.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0)
-    is_last = __hip_atomic_fetch_add(&P.counters[sh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __shared__ float merge_m[kMergeCap], merge_w[kMergeCap];
-  merge_partials<ACT, D, NW * 64>(P, sh, 1, pf.pre, nparts, tid, merge_m, merge_w);
-  if (tid == 0) __hip_atomic_store(&P.counters[sh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The merge after a decode launch: one wave per (q head, sequence) merges
+// the head's partials, a shared prefix's included, exactly:
+//   out = sum_q 2^(m_q - M) o_q / sum_q 2^(m_q - M) l_q,  M = max_q m_q
+// (the online softmax's rescaling).  Heads with a single partial were
+// written by the decode.  Lane q holds partial q's (m, l) (lanes stride
+// over longer lists).  The (m, l) of the first 64 slots and the vectors of
+// the first QB are loaded together with the context length, before the
+// number of partials is known (every slot of the head's workspace row
+// exists; slots past the partials are read and ignored), so a head with few
+// partials costs one memory round trip.  Lane i takes elements
+// E i .. E i + E - 1.
+template <typename ACT, int D>
+__global__ __launch_bounds__(64) void merge_kernel(const DecodeParams P) {
+  constexpr int E = D >= 64 ? D / 64 : 1;  // elements per lane (head_dim 32: lanes 32..63 idle)
+  constexpr int QB = 8;                    // partials per batch of vector loads
+  const int h = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const int64_t sh = static_cast<int64_t>(s) * P.hq + h;
+  // the head's workspace row (written by earlier launches; coherent loads
+  // all the same)
+  const int slots = P.max_parts;
+  const CoherentWindow wml(P.ws_ml + sh * slots * 2, static_cast<uint32_t>(slots) * 8u);
+  const CoherentWindow wo(P.ws_o + sh * slots * D, static_cast<uint32_t>(slots) * (D * 4u));
+  const bool active = lane * E < D;
+  auto load_o = [&](int q, float (&x)[E]) {
+    const uint32_t off = static_cast<uint32_t>(q * D + lane * E) * 4u;
+    if constexpr (E == 2) {
+      const float2_t v = wo.load2(off);
+      x[0] = v[0];
+      x[1] = v[1];
+    } else {
+      x[0] = wo.load1(off);
+    }
+  };
+  float x[QB][E];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+    if (qb < slots && active) load_o(qb, x[qb]);
+  float2_t mlq = {-INFINITY, 0.f};
+  if (lane < slots) mlq = wml.load2(static_cast<uint32_t>(lane) * 8u);
+  const int ctx = P.ctx[s];
+  const SeqPrefix pf = seq_prefix(P, s);
+  const bool bad_len = seq_bad_len(P, ctx, pf);
+  const int nparts = bad_len ? 1 : max(1, (ctx - pf.begin + kPartitionTokens - 1) / kPartitionTokens);
+  const int total = pf.pre + nparts;
+  if (bad_len || total == 1) return;
+  if (lane >= total) mlq = float2_t{-INFINITY, 0.f};
+  float M = mlq[0];
+  for (int q = lane + 64; q < total; q += 64) M = fmaxf(M, wml.load1(static_cast<uint32_t>(q) * 8u));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float wq = lane < total ? exp2f(mlq[0] - M) : 0.f;  // partial `lane`'s weight
+  float L = wq * mlq[1];
+  for (int q = lane + 64; q < total; q += 64) {
+    const float2_t v = wml.load2(static_cast<uint32_t>(q) * 8u);
+    L += exp2f(v[0] - M) * v[1];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int q0 = 0; q0 < total; q0 += QB) {
+    if (q0 > 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        if (q0 + qb < total && active) load_o(q0 + qb, x[qb]);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int q = q0 + qb;
+      if (q >= total) break;
+      const float w = q < 64 ? __shfl(wq, q) : exp2f(wml.load1(static_cast<uint32_t>(q) * 8u) - M);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += w * x[qb][e];
+    }
+  }
+  if (active) {
+    ACT* out = static_cast<ACT*>(P.out);
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < E; ++e) out[sh * D + lane * E + e] = from_f32<ACT>(acc[e] * inv);
+  }
 }
 
 template <typename KV, typename ACT, int D>
@@ -489,14 +518,15 @@ hipError_t decode_t(const DecodeArgs& a) {
   const DecodeParams P = make_decode_params(a);
   const unsigned np = static_cast<unsigned>(decode_grid_parts(a, kPartitionTokens));
   const dim3 grid(PA_GRID_HEAD_FIRST ? a.num_q_heads : np, PA_GRID_HEAD_FIRST ? np : a.num_q_heads, a.num_seqs);
-  auto kern = a.ngroups > 0
-                  ? (c.block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true, true>
-                                         : decode_kernel<KV, ACT, D, NW, U, false, true>)
-                  : (c.block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true, false>
-                                         : decode_kernel<KV, ACT, D, NW, U, false, false>);
+  auto kern = c.block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true> : decode_kernel<KV, ACT, D, NW, U, false>;
   if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, a.stream, P);
-  const hipError_t e = hipGetLastError();
+  hipError_t e = hipGetLastError();
+  // partials exist only where a head has more than one
+  if (e == hipSuccess && (np > 1 || a.ngroups > 0)) {
+    hipLaunchKernelGGL((merge_kernel<ACT, D>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0, a.stream, P);
+    e = hipGetLastError();
+  }
   if (a.ev[1]) (void)hipEventRecord(a.ev[1], a.stream);
   return e;
 }

@@ -54,6 +54,14 @@ __device__ __forceinline__ SeqPrefix seq_prefix(const DecodeParams& P, int s) {
   return SeqPrefix{0, 0};
 }
 
+// A context length the launch cannot serve (negative, past max_context_len
+// or the table, shorter than the sequence's shared prefix, or a new token
+// inside that prefix): the sequence's output is NaN.
+__device__ __forceinline__ bool seq_bad_len(const DecodeParams& P, int ctx, const SeqPrefix& pf) {
+  return ctx < 0 || ctx > P.max_ctx || static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) << P.log2_bs ||
+         ctx < pf.begin || (P.k_new != nullptr && pf.pre > 0 && ctx - 1 < pf.begin);
+}
+
 inline DecodeParams make_decode_params(const DecodeArgs& a) {
   const pa_kv_cache& c = *a.cache;
   DecodeParams P;
@@ -120,6 +128,9 @@ struct CoherentWindow {
   __device__ __forceinline__ float4_t load4(uint32_t off) const {
     return __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
   }
+  __device__ __forceinline__ float load1(uint32_t off) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSc1));
+  }
   __device__ __forceinline__ float2_t load2(uint32_t off) const {
     return __builtin_bit_cast(float2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kSc1));
   }
@@ -182,9 +193,10 @@ namespace pa {
 
 // The merged state of a shared prefix: the prefix pass left `pre` partials
 // of workspace row sh in slots 0 .. pre - 1, each (m, l) and an unnormalised
-// vector (without the V scale).  Returns the running max M (log2 units), the
-// weight sum L and elements [d0, d0 + N) of the vector, rescaled to M; a
-// decode partition starts its online softmax from them.  Coherent loads:
+// vector times the V scale, like every partial.  Returns the running max M
+// (log2 units), the weight sum L and elements [d0, d0 + N) of the vector,
+// rescaled to M and without the V scale (in the pool's units, as a decode
+// partition accumulates); the partition starts its online softmax from them.  Coherent loads:
 // another launch wrote the partials, possibly from another XCD.
 template <int D, int N>
 __device__ __forceinline__ void load_prefix_state(const DecodeParams& P, int64_t sh, int pre, int d0, float& M,
@@ -203,6 +215,8 @@ __device__ __forceinline__ void load_prefix_state(const DecodeParams& P, int64_t
 #pragma unroll
     for (int e = 0; e < N; ++e) o[e] += w * coherent_load(src + e);
   }
+#pragma unroll
+  for (int e = 0; e < N; ++e) o[e] /= P.v_scale;
 }
 
 // Floats of LDS scratch merge_partials needs (two arrays of this size); at

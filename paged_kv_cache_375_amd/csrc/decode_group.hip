@@ -122,8 +122,10 @@ struct Layout {
 // 16 * HT of them; the shared blocks, read through the table of the group's
 // first sequence, are loaded once for all of those rows.  Each partition of
 // kPrefixPartTokens tokens leaves (m, l, o) partials in workspace slot p of
-// every row (o without the V scale); the first partition of the decode
-// launch that follows starts its online softmax from their merged state.
+// every row (o times the V scale, like every partial).  The grouped decode
+// launch that follows starts the online softmax of each head's first
+// partition from their merged state; after the per-head decode, its merge
+// launch takes them with the decode's own partials.
 template <typename KV, int D, int HT, int NW, bool UNI, bool PREFIX>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_occupancy<D, HT>()))) void decode_group_kernel(const DecodeParams P, int groups_per_kv) {
   using L = Layout<KV, D>;
@@ -165,8 +167,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
     ctx = P.ctx[s];
     // tokens [0, begin) of a shared prefix were covered by the prefix pass
     pf = seq_prefix(P, s);
-    bad_len = ctx < 0 || ctx > P.max_ctx || static_cast<int64_t>(ctx) > static_cast<int64_t>(P.max_blocks) * bs ||
-              ctx < pf.begin || (P.k_new != nullptr && pf.pre > 0 && ctx - 1 < pf.begin);
+    bad_len = seq_bad_len(P, ctx, pf);
     const int part = P.part_tokens;  // a multiple of kPartitionTokens, chosen per launch
     // this launch's partitions; partition 0 starts from a shared prefix's
     // merged state, so these are all the partials to merge
@@ -555,9 +556,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
           for (int i = 0; i < 4; ++i) r[i] = static_cast<_Float16>(bad ? NAN : o[ht][dt][i] * f);
           *reinterpret_cast<half4_t*>(out + sh * D + d) = r;
         } else if (PREFIX) {
-          // read by a later launch: plain 16-byte stores, without the V scale
+          // read by a later launch: plain 16-byte stores, V-scaled like
+          // every partial
           const float4_t nan4 = {NAN, NAN, NAN, NAN};
-          *reinterpret_cast<float4_t*>(P.ws_o + (sh * P.max_parts + slot) * D + d) = bad ? nan4 : o[ht][dt];
+          *reinterpret_cast<float4_t*>(P.ws_o + (sh * P.max_parts + slot) * D + d) =
+              bad ? nan4 : o[ht][dt] * P.v_scale;
         } else {
           const float4_t nan4 = {NAN, NAN, NAN, NAN};
           wso.store4(static_cast<uint32_t>(hh * static_cast<int64_t>(P.max_parts) * D + d) * 4u,
