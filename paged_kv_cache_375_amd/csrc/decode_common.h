@@ -30,6 +30,8 @@ struct DecodeParams {
   int num_blocks, log2_bs, hkv, hq, group, max_blocks, max_ctx;
   int max_parts;    // partitions of kPartitionTokens the workspace holds per head (its stride)
   int part_tokens;  // tokens per partition in this launch: a multiple of kPartitionTokens
+  int num_seqs;
+  int fold_order;   // grouped decode: dispatch sequences in folded length order (see the kernel)
   // scores are kept in log2 units: score_scale = sm_scale * log2(e) (* k_scale
   // for FP8 pools); v_scale multiplies the output (FP8 pools, else 1)
   float score_scale, v_scale, k_inv, v_inv;
@@ -87,6 +89,8 @@ inline DecodeParams make_decode_params(const DecodeArgs& a) {
   P.max_ctx = a.max_ctx;
   P.max_parts = a.max_parts;
   P.part_tokens = kPartitionTokens;
+  P.num_seqs = a.num_seqs;
+  P.fold_order = 0;
   P.score_scale = a.sm_scale * kLog2e * (c.kv_dtype == PA_FP8_E4M3 ? c.k_scale : 1.f);
   P.v_scale = c.kv_dtype == PA_FP8_E4M3 ? c.v_scale : 1.f;
   P.k_inv = c.k_inv_scale;

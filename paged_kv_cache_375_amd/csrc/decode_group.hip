@@ -164,6 +164,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
     kvh = blockIdx.x / groups_per_kv;
     s = blockIdx.y;
     p = blockIdx.z;
+    if (P.fold_order) {
+      // A launch of one partition per (sequence, KV head, group) that fills
+      // two workgroups per CU in one round: workgroups i and i + (CUs) share
+      // a CU, i.e. sequence positions y and y + B / 2.  Position y takes the
+      // y-th longest sequence in the first half and the y-th shortest in the
+      // second, so each CU holds a long and a short one and all CUs finish
+      // together.  Ranks order by length, then index (a permutation).
+      __shared__ int lens[kFoldMaxSeqs];
+      __shared__ int pick;
+      const int B = P.num_seqs, half = (B + 1) / 2;
+      const int want = s < half ? s : B - 1 - (s - half);
+      if (threadIdx.x < B) lens[threadIdx.x] = P.ctx[threadIdx.x];
+      __syncthreads();
+      if (static_cast<int>(threadIdx.x) < B) {
+        const int c = lens[threadIdx.x];
+        int rank = 0;
+        for (int u = 0; u < B; ++u) rank += lens[u] > c || (lens[u] == c && u < static_cast<int>(threadIdx.x));
+        if (rank == want) pick = threadIdx.x;
+      }
+      __syncthreads();
+      s = __builtin_amdgcn_readfirstlane(pick);
+    }
     ctx = P.ctx[s];
     // tokens [0, begin) of a shared prefix were covered by the prefix pass
     pf = seq_prefix(P, s);
@@ -630,6 +652,9 @@ hipError_t launch_ht(const DecodeArgs& a, int groups) {
   DecodeParams P = make_decode_params(a);
   P.part_tokens = part;
   const int grid_parts = decode_grid_parts(a, part);
+  // one partition per unit, all resident at once: balance CUs by length
+  P.fold_order = grid_parts == 1 && a.num_seqs >= 2 && a.num_seqs <= kFoldMaxSeqs &&
+                 units <= static_cast<int64_t>(slots);
   // Dispatch order runs over (KV head, group), then sequences, then
   // partitions: consecutive workgroups go to different XCDs, so every
   // partition index (the first ones are the longest and the only ones

@@ -74,6 +74,10 @@ inline int decode_grid_parts(const DecodeArgs& a, int part) {
 // kTabEntries blocks.
 constexpr int kTabEntries = 1024;
 
+// Most sequences a grouped decode launch dispatches in folded length order
+// (each workgroup ranks every context length in LDS).
+constexpr int kFoldMaxSeqs = 256;
+
 // Workgroups of `threads` threads of `kernel` the current device holds at
 // once (compute units x workgroups per unit; cached per kernel and device);
 // 0 if the device cannot be queried.
