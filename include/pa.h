@@ -403,7 +403,9 @@ const char* pa_last_error(void);
  * kernel runs on.  pa_timing_read synchronises those events and returns the
  * summed milliseconds and the number of launches since the last read, then
  * resets the sums.  Events are created on enable (up to 4096 launches are
- * kept between reads) and destroyed on disable.  Not thread-safe.
+ * kept between reads) and destroyed on disable.  They carry no system-scope
+ * memory fence, so they perturb the timed launches as little as possible;
+ * they order nothing for the caller.  Not thread-safe.
  */
 pa_status pa_timing_enable(int32_t on);
 pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches);

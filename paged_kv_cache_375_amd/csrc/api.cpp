@@ -339,7 +339,10 @@ extern "C" pa_status pa_timing_enable(int32_t on) {
   if (!on) return ok();
   g_timing.part_ev.resize(2 * kTimingSlots);
   for (hipEvent_t& e : g_timing.part_ev) {
-    hipError_t r = hipEventCreate(&e);
+    // Timing only: no system-scope fence (cache writeback and invalidation)
+    // when an event completes, which would otherwise add several
+    // microseconds between the kernels it brackets and the next launch.
+    hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
     if (r != hipSuccess) {
       e = nullptr;
       timing_release();

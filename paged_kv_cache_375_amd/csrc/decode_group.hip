@@ -164,6 +164,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
     kvh = blockIdx.x / groups_per_kv;
     s = blockIdx.y;
     p = blockIdx.z;
+    int ctx_ranked = 0;
     if (P.fold_order) {
       // A launch of one partition per (sequence, KV head, group) that fills
       // two workgroups per CU in one round: workgroups i and i + (CUs) share
@@ -185,8 +186,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
       }
       __syncthreads();
       s = __builtin_amdgcn_readfirstlane(pick);
+      ctx_ranked = __builtin_amdgcn_readfirstlane(lens[s]);  // no second global read
     }
-    ctx = P.ctx[s];
+    ctx = P.fold_order ? ctx_ranked : P.ctx[s];
     // tokens [0, begin) of a shared prefix were covered by the prefix pass
     pf = seq_prefix(P, s);
     bad_len = seq_bad_len(P, ctx, pf);
