@@ -103,8 +103,8 @@ def oracle_decode_threaded(ref, threads):
 
 
 def host_threads():
-    """Host threads the CPU baseline may use: this process's CPUs, at most 16
-    (a one-GPU share of the host)."""
+    """Host threads the CPU baseline uses: the CPUs this process may run on,
+    at most 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
