@@ -1,0 +1,68 @@
+"""Long and maximum contexts (needs an MI355X).
+
+Contexts far past one launch's partitions exercise the merges at their
+largest: the per-head kernel's merge launch with more than 64 partials per
+head (its lanes then loop over the partials), the grouped kernel's in-launch
+merge over hundreds of partitions, and the longest context the library
+accepts (1024 partitions of 512 tokens).  Every output element is checked
+against the reference; the pool after the step is bit-exact."""
+import numpy as np
+import pytest
+
+from paged_kv_cache_375_amd import api
+from paged_kv_cache_375_amd._lib import PagedAttnError
+from paged_kv_cache_375_amd.workloads import Workload
+from tests.gpu_helpers import TOL, build_pair, out_f64, pool_bytes
+
+pytestmark = pytest.mark.gpu
+
+MAX_CONTEXT = 1024 * 512  # the library's limit on max_context_len
+
+CASES = {
+    # per-head kernel, f16: 79 to 137 partials per head
+    "per_head_f16": Workload("long_mha_f16", 4, 4, 128, 16, 2, 40000, 70000),
+    # per-head kernel, FP8 pool: 65 to 79 partials per head
+    "per_head_e4m3": Workload("long_mha_e4m3", 2, 2, 128, 16, 2, 33000, 40000, kv="e4m3"),
+    # grouped kernel (G 8), hundreds of partitions merged in the launch
+    "grouped_f16": Workload("long_gqa_f16", 16, 2, 128, 16, 2, 40000, 70000),
+    # grouped kernel, MQA shape with 4-token blocks
+    "grouped_mqa_bs4": Workload("long_mqa_bs4", 71, 1, 64, 4, 1, 60000, 60000),
+    # the longest context accepted, per-head and grouped
+    "max_per_head": Workload("max_mha", 1, 1, 32, 16, 1, MAX_CONTEXT, MAX_CONTEXT),
+    "max_grouped": Workload("max_gqa", 2, 1, 32, 16, 1, MAX_CONTEXT, MAX_CONTEXT),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_long_context_parity(name):
+    wl = CASES[name]
+    print(f"[long] {name}: building {wl}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    assert gpu.max_ctx <= MAX_CONTEXT
+    out = out_f64(gpu.run())
+    print(f"[long] {name}: reference", flush=True)
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    want = ref.decode()
+    err = float(np.max(np.abs(out - want)))
+    print(f"[long] {name}: contexts {dr.ctx.tolist()}, max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]
+    # Over tens of thousands of tokens the outputs are averages of many V rows
+    # and small (max |out| ~ 1e-2), so the absolute bound says little; the
+    # error must also stay within a few f16 roundings (2^-11 relative) of the
+    # largest output: 2e-3 of it for f16 pools, 5e-3 for FP8 pools (whose
+    # scales enter the GPU's arithmetic at other points).
+    rel = 2e-3 if wl.kv != "e4m3" else 5e-3
+    assert err <= rel * float(np.max(np.abs(want)))
+    # the step again: same output, bit for bit
+    assert np.array_equal(out, out_f64(gpu.run()))
+
+
+def test_context_past_the_limit_is_refused_before_any_launch():
+    wl = CASES["max_per_head"]
+    dr, gpu, _ = build_pair(wl)
+    with pytest.raises(PagedAttnError) as e:
+        api.decode(gpu.cache, gpu.q, gpu.tables, gpu.ctx, MAX_CONTEXT + 1, gpu.sm_scale)
+    assert "max_context_len" in str(e.value)
