@@ -75,6 +75,10 @@ WORKLOADS = {
     # first write of every sequence hits a partially filled shared block
     "opt13b_fp8_prefix505": Workload("opt13b_fp8_prefix505", 40, 40, 128, 16, 64, 1, 1536,
                                      kv="e4m3", prefix_len=505),
+    # one GPU's share under tensor parallelism over 8 GPUs (heads split, the
+    # same sequences, lengths and block tables on every GPU)
+    "llama70b_gqa_tp8": Workload("llama70b_gqa_tp8", 8, 1, 128, 16, 64, 1024, 4096),
+    "opt13b_tp8": Workload("opt13b_tp8", 5, 5, 128, 16, 30, 128, 2048),
 }
 
 BLOCK_SIZE_SWEEP = (1, 2, 4, 8, 16, 32, 64)

@@ -110,7 +110,7 @@ def test_group_kernel_special_cases():
     assert torch.count_nonzero(out0) == 0
 
 
-FULL = ["opt13b", "llama70b_gqa", "falcon7b_mqa", "opt13b_fp8_prefix"]
+FULL = ["opt13b", "llama70b_gqa", "falcon7b_mqa", "opt13b_fp8_prefix", "llama70b_gqa_tp8", "opt13b_tp8"]
 
 
 @pytest.mark.parametrize("name", FULL)
