@@ -35,6 +35,13 @@
  * memory in these calls and keeps no device pointer between calls.  The
  * allocator object is the only library-owned state.
  *
+ * Graph capture: the decode, append, prompt-write and block-copy calls only
+ * launch kernels on the given stream (no memset, no allocation, no host
+ * synchronisation), so a stream being captured into a HIP graph records
+ * them, and the graph can be replayed; the workspace's arrival counters are
+ * back at zero after every launch.  Timing events (pa_timing_enable) are for
+ * measurement and should be off while capturing.
+ *
  * Supported shapes: head_dim in {32, 64, 128}; block_size a power of two in
  * 1..64; num_q_heads a multiple of num_kv_heads; kv dtype f32, f16 or
  * FP8 E4M3; activation dtype f32 or f16 (f32 only with an f32 pool).
