@@ -30,6 +30,10 @@ GROUP_CASES = [
     (64, 8, 128, "e4m3", 16),  # FP8 pool, head_dim 128
     (40, 4, 64, "e4m3", 8),    # FP8 pool, head_dim 64
     (12, 3, 32, "e4m3", 16),   # FP8 pool, head_dim 32 (8-byte K loads)
+    # many head tiles per KV head, more pool dtypes and head sizes
+    (71, 1, 64, "e4m3", 16),   # FP8 pool, five tiles
+    (80, 2, 128, "e4m3", 16),  # FP8 pool, G 40, head_dim 128: three tiles
+    (64, 1, 128, "f16", 64),   # G 64, head_dim 128: four tiles, 64-token blocks
 ]
 
 
@@ -88,15 +92,17 @@ def test_group_kernel_placement_invariance_bit_exact():
     assert torch.equal(out, out2)
 
 
-def test_group_kernel_special_cases():
+@pytest.mark.parametrize("hq,hkv,d", [(64, 8, 128), (71, 1, 64)], ids=["gqa", "mqa"])
+def test_group_kernel_special_cases(hq, hkv, d):
     from paged_kv_cache_375_amd import api
-    wl = Workload("group_ctx1", 64, 8, 128, 16, 4, 1, 1)
+    G = hq // hkv
+    wl = Workload("group_ctx1", hq, hkv, d, 16, 4, 1, 1)
     dr, gpu, ref = build_pair(wl)
     out = gpu.run()
     torch.cuda.synchronize()
     # one token: its weight is exactly one, the output is the appended V
-    assert torch.equal(out, gpu.v_new.repeat_interleave(8, dim=1))
-    wl = Workload("group_bad", 64, 8, 128, 16, 3, 300, 1100)
+    assert torch.equal(out, gpu.v_new.repeat_interleave(G, dim=1))
+    wl = Workload("group_bad", hq, hkv, d, 16, 3, 300, 1100)
     dr, gpu, ref = build_pair(wl)
     gpu.run()
     bad = gpu.tables.clone()

@@ -27,6 +27,8 @@ CASES = {
     "grouped_f16": Workload("long_gqa_f16", 16, 2, 128, 16, 2, 40000, 70000),
     # grouped kernel, MQA shape with 4-token blocks
     "grouped_mqa_bs4": Workload("long_mqa_bs4", 71, 1, 64, 4, 1, 60000, 60000),
+    # grouped kernel, MQA shape with 16-token blocks (tiles read as whole blocks)
+    "grouped_mqa_bs16": Workload("long_mqa_bs16", 71, 1, 64, 16, 1, 60000, 60000),
     # the longest context accepted, per-head and grouped
     "max_per_head": Workload("max_mha", 1, 1, 32, 16, 1, MAX_CONTEXT, MAX_CONTEXT),
     "max_grouped": Workload("max_gqa", 2, 1, 32, 16, 1, MAX_CONTEXT, MAX_CONTEXT),
