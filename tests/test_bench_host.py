@@ -32,3 +32,32 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_traffic_summary_is_used_only_for_the_kernels_it_measured(monkeypatch):
+    """The HBM traffic figure comes from a committed counter summary that
+    names the kernel sources it measured (a hash); once the sources differ
+    it is reported as unknown rather than carried over."""
+    rec = bench.measured_traffic("opt13b", 0)
+    import json
+    import os
+    path = os.path.join(bench.ROOT, "profiles", "decode_kernel_opt13b_traffic.json")
+    stored = json.load(open(path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: stored["kernel_source_sha"])
+    assert bench.measured_traffic("opt13b", 0) == stored["hbm_bytes_per_launch"]
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.measured_traffic("opt13b", 0) is None
+    assert bench.measured_traffic("no_such_workload", 0) is None
+    assert rec is None or rec == stored["hbm_bytes_per_launch"]
+
+
+def test_kernel_source_hash_covers_every_kernel_source():
+    import hashlib
+    import os
+    csrc = os.path.join(bench.ROOT, "paged_kv_cache_375_amd", "csrc")
+    files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    assert "decode.hip" in files and "decode_group.hip" in files and "decode_common.h" in files
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    assert bench.kernel_source_hash() == h.hexdigest()[:16]
