@@ -268,6 +268,9 @@ def main():
                          "block size (the workload's heads, head_dim and pool dtype)")
     args = ap.parse_args()
 
+    if args.steps < 1 or args.warmup < 0:
+        print(f"bench.py needs --steps >= 1 and --warmup >= 0; got {args.steps}, {args.warmup}", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
