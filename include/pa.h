@@ -53,6 +53,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Every entry point is noexcept for C++ callers: no exception leaves the
+ * library (an allocation failure inside it ends the process). */
+#ifdef __cplusplus
+#define PA_NOEXCEPT noexcept
+#else
+#define PA_NOEXCEPT
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -108,7 +116,7 @@ typedef struct {
  */
 pa_status pa_kv_append(const pa_kv_cache* cache, const void* k_new, const void* v_new, int32_t act,
                        const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                       int32_t max_blocks_per_seq, void* stream);
+                       int32_t max_blocks_per_seq, void* stream) PA_NOEXCEPT;
 
 /*
  * pa_kv_write_prompt — the prompt phase: a sequence's whole prompt K/V are
@@ -127,7 +135,7 @@ pa_status pa_kv_append(const pa_kv_cache* cache, const void* k_new, const void* 
 pa_status pa_kv_write_prompt(const pa_kv_cache* cache, const void* k_src, const void* v_src, int32_t act,
                              const int64_t* src_row, const int32_t* start_pos, const int32_t* count,
                              const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
-                             int32_t max_count, void* stream);
+                             int32_t max_count, void* stream) PA_NOEXCEPT;
 
 /*
  * pa_copy_blocks — the copy of copy-on-write: before a sequence writes into
@@ -140,7 +148,7 @@ pa_status pa_kv_write_prompt(const pa_kv_cache* cache, const void* k_src, const 
  * with an id outside [0, num_blocks) are skipped.  Destinations must be
  * distinct and no destination may be a source.
  */
-pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst_pairs, int32_t n, void* stream);
+pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst_pairs, int32_t n, void* stream) PA_NOEXCEPT;
 
 /*
  * pa_swap_blocks — the copy of preemption by swapping: a preempted
@@ -161,7 +169,7 @@ pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst_pairs,
  */
 typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_direction;
 pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, const int32_t* block_ids, int32_t n,
-                         int32_t direction, void* stream);
+                         int32_t direction, void* stream) PA_NOEXCEPT;
 
 /*
  * pa_decode_workspace_size — bytes of device workspace pa_decode and
@@ -171,7 +179,7 @@ pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, c
  * partition).  0 when every context fits one partition (512 tokens).
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                int32_t max_context_len);
+                                int32_t max_context_len) PA_NOEXCEPT;
 
 /*
  * pa_decode — one generation step's attention: for every sequence s and
@@ -213,7 +221,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
 pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* out, int32_t act, int32_t num_q_heads,
                     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                     int32_t max_blocks_per_seq, int32_t max_context_len, float sm_scale,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                    void* workspace, size_t workspace_bytes, void* stream) PA_NOEXCEPT;
 
 /*
  * pa_decode_step — the whole generation step in one launch: the result of
@@ -230,7 +238,7 @@ pa_status pa_decode_step(const pa_kv_cache* cache, const void* q, const void* k_
                          void* out, int32_t act, int32_t num_q_heads, const int32_t* block_tables,
                          const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                          int32_t max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
-                         void* stream);
+                         void* stream) PA_NOEXCEPT;
 
 /*
  * pa_decode_shared_prefix — decode (and, with k_new/v_new non-NULL, the
@@ -261,9 +269,9 @@ pa_status pa_decode_shared_prefix(const pa_kv_cache* cache, const void* q, const
                                   const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                                   int32_t max_context_len, float sm_scale, int32_t num_groups,
                                   const int32_t* group_start, const int32_t* group_shared_blocks, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+                                  size_t workspace_bytes, void* stream) PA_NOEXCEPT;
 size_t pa_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                       int32_t max_context_len, int32_t max_shared_tokens);
+                                       int32_t max_context_len, int32_t max_shared_tokens) PA_NOEXCEPT;
 
 /* ============================== host allocator ============================= */
 /*
@@ -294,11 +302,11 @@ typedef struct {
 /* free_order: host int32 [num_blocks], a permutation giving the initial free
  * list order (NULL = 0, 1, ..., num_blocks - 1). */
 pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
-                              pa_allocator** out);
-void pa_allocator_destroy(pa_allocator* a);
-int32_t pa_allocator_num_free(const pa_allocator* a);
+                              pa_allocator** out) PA_NOEXCEPT;
+void pa_allocator_destroy(pa_allocator* a) PA_NOEXCEPT;
+int32_t pa_allocator_num_free(const pa_allocator* a) PA_NOEXCEPT;
 /* A new sequence holding num_tokens (>= 0) tokens: ceil(n / block_size) blocks. */
-pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens);
+pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens) PA_NOEXCEPT;
 /*
  * Automatic prefix caching [F55 §后来的做法]: allocate a sequence whose
  * prompt is tokens[0, num_tokens) (host int32 token ids), reusing blocks
@@ -320,17 +328,17 @@ pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens);
  * are not keyed.
  */
 pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const int32_t* tokens, int32_t num_tokens,
-                                 int32_t* num_cached_tokens);
+                                 int32_t* num_cached_tokens) PA_NOEXCEPT;
 /* Number of blocks that currently hold a prefix-cache key (-1 if a is NULL). */
-int32_t pa_prefix_cache_size(const pa_allocator* a);
+int32_t pa_prefix_cache_size(const pa_allocator* a) PA_NOEXCEPT;
 /* child shares every block of parent (reference counts + 1). */
-pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child);
+pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child) PA_NOEXCEPT;
 /* Reserve the slot of one more token.  *cow_src / *cow_dst receive the block
  * copy the caller must perform (pa_copy_blocks) before writing, or -1 / -1. */
-pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* cow_src, int32_t* cow_dst);
+pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* cow_src, int32_t* cow_dst) PA_NOEXCEPT;
 /* Release the sequence: reference counts - 1, unreferenced blocks are freed
  * (a swapped-out sequence is simply forgotten). */
-pa_status pa_seq_free(pa_allocator* a, int32_t seq);
+pa_status pa_seq_free(pa_allocator* a, int32_t seq) PA_NOEXCEPT;
 /*
  * Preemption by swapping: when blocks run out, the latest arrival gives up
  * all of its blocks, which may be moved to host memory and moved back when
@@ -348,19 +356,19 @@ pa_status pa_seq_free(pa_allocator* a, int32_t seq);
  * smaller.  A swapped-out sequence keeps its place in arrival order but is
  * not a preemption candidate; pa_seq_get, append and fork do not see it.
  */
-pa_status pa_seq_swap_out(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap, int32_t* num_blocks);
-pa_status pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap, int32_t* num_blocks);
+pa_status pa_seq_swap_out(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap, int32_t* num_blocks) PA_NOEXCEPT;
+pa_status pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap, int32_t* num_blocks) PA_NOEXCEPT;
 /* Copy the table (up to cap entries) and report its length and context. */
 pa_status pa_seq_get(const pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
-                     int32_t* num_blocks, int32_t* context_len);
+                     int32_t* num_blocks, int32_t* context_len) PA_NOEXCEPT;
 /* Host int32 tables [n][max_blocks_per_seq] (padding -1) and lengths [n]. */
 pa_status pa_export_tables(const pa_allocator* a, const int32_t* seqs, int32_t n,
-                           int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out);
-int32_t pa_block_refcount(const pa_allocator* a, int32_t block);
-pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out);
+                           int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out) PA_NOEXCEPT;
+int32_t pa_block_refcount(const pa_allocator* a, int32_t block) PA_NOEXCEPT;
+pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out) PA_NOEXCEPT;
 /* The sequence to preempt first when blocks run out: the latest arrival
  * among those holding blocks [F55 §放不下的时候]; -1 if none. */
-int32_t pa_latest_arrival(const pa_allocator* a);
+int32_t pa_latest_arrival(const pa_allocator* a) PA_NOEXCEPT;
 
 /*
  * The toy machine's arrival simulator [F55 §实验台], run over this
@@ -396,13 +404,13 @@ typedef struct {
 } pa_arrival_readout;
 pa_status pa_simulate_arrivals(int32_t num_blocks, int32_t block_size, const int32_t* arrivals,
                                const int32_t* lengths, int32_t n, pa_arrival_readout* out, int32_t* trace,
-                               int32_t trace_cap);
+                               int32_t trace_cap) PA_NOEXCEPT;
 
 /* ================================ utilities ================================ */
 
-const char* pa_status_str(pa_status s);
+const char* pa_status_str(pa_status s) PA_NOEXCEPT;
 /* Detail of the last non-OK status returned on this thread (never NULL). */
-const char* pa_last_error(void);
+const char* pa_last_error(void) PA_NOEXCEPT;
 
 /*
  * Kernel timing for measurement: while enabled, every pa_decode and
@@ -414,8 +422,8 @@ const char* pa_last_error(void);
  * memory fence, so they perturb the timed launches as little as possible;
  * they order nothing for the caller.  Not thread-safe.
  */
-pa_status pa_timing_enable(int32_t on);
-pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches);
+pa_status pa_timing_enable(int32_t on) PA_NOEXCEPT;
+pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches) PA_NOEXCEPT;
 
 #ifdef __cplusplus
 }

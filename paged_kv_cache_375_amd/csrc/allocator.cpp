@@ -113,7 +113,7 @@ using pa::fail;
 using pa::ok;
 
 extern "C" pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
-                                         pa_allocator** out) {
+                                         pa_allocator** out) noexcept {
   if (!out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: out is NULL");
   *out = nullptr;
   if (num_blocks < 0 || block_size < 1)
@@ -145,13 +145,13 @@ extern "C" pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
   return ok();
 }
 
-extern "C" void pa_allocator_destroy(pa_allocator* a) { delete a; }
+extern "C" void pa_allocator_destroy(pa_allocator* a) noexcept { delete a; }
 
-extern "C" int32_t pa_allocator_num_free(const pa_allocator* a) {
+extern "C" int32_t pa_allocator_num_free(const pa_allocator* a) noexcept {
   return a ? a->nfree : -1;
 }
 
-extern "C" pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens) {
+extern "C" pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_tokens) noexcept {
   if (!a || seq < 0 || num_tokens < 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_allocate: bad argument (seq %d, tokens %d)", seq, num_tokens);
   if (a->exists(seq)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_allocate: sequence %d exists", seq);
@@ -169,7 +169,7 @@ extern "C" pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_t
 }
 
 extern "C" pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const int32_t* tokens,
-                                            int32_t num_tokens, int32_t* num_cached_tokens) {
+                                            int32_t num_tokens, int32_t* num_cached_tokens) noexcept {
   static const char* fn = "pa_seq_allocate_cached";
   if (!a || seq < 0 || num_tokens < 0 || !num_cached_tokens || (num_tokens > 0 && !tokens))
     return fail(PA_ERR_INVALID_ARGUMENT, "%s: bad argument (seq %d, tokens %d)", fn, seq, num_tokens);
@@ -230,11 +230,11 @@ extern "C" pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const 
   return ok();
 }
 
-extern "C" int32_t pa_prefix_cache_size(const pa_allocator* a) {
+extern "C" int32_t pa_prefix_cache_size(const pa_allocator* a) noexcept {
   return a ? static_cast<int32_t>(a->cache.size()) : -1;
 }
 
-extern "C" pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child) {
+extern "C" pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child) noexcept {
   if (!a || child < 0) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_fork: bad argument");
   auto it = a->seqs.find(parent);
   if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_fork: unknown parent %d", parent);
@@ -246,7 +246,7 @@ extern "C" pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child)
   return ok();
 }
 
-extern "C" pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* cow_src, int32_t* cow_dst) {
+extern "C" pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* cow_src, int32_t* cow_dst) noexcept {
   if (!a || !cow_src || !cow_dst) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_append_slot: NULL argument");
   *cow_src = -1;
   *cow_dst = -1;
@@ -276,7 +276,7 @@ extern "C" pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* c
   return ok();
 }
 
-extern "C" pa_status pa_seq_free(pa_allocator* a, int32_t seq) {
+extern "C" pa_status pa_seq_free(pa_allocator* a, int32_t seq) noexcept {
   if (!a) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_free: NULL allocator");
   auto sw = a->swapped.find(seq);
   if (sw != a->swapped.end()) {
@@ -293,7 +293,7 @@ extern "C" pa_status pa_seq_free(pa_allocator* a, int32_t seq) {
 }
 
 extern "C" pa_status pa_seq_swap_out(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
-                                     int32_t* num_blocks) {
+                                     int32_t* num_blocks) noexcept {
   if (!a || !num_blocks || cap < 0 || (cap > 0 && !block_ids))
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_swap_out: bad argument");
   auto it = a->seqs.find(seq);
@@ -310,7 +310,7 @@ extern "C" pa_status pa_seq_swap_out(pa_allocator* a, int32_t seq, int32_t* bloc
 }
 
 extern "C" pa_status pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
-                                    int32_t* num_blocks) {
+                                    int32_t* num_blocks) noexcept {
   if (!a || !num_blocks || cap < 0 || (cap > 0 && !block_ids))
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_swap_in: bad argument");
   auto sw = a->swapped.find(seq);
@@ -334,7 +334,7 @@ extern "C" pa_status pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* block
 }
 
 extern "C" pa_status pa_seq_get(const pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
-                                int32_t* num_blocks, int32_t* context_len) {
+                                int32_t* num_blocks, int32_t* context_len) noexcept {
   if (!a || cap < 0 || (cap > 0 && !block_ids)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_get: bad argument");
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_get: unknown sequence %d", seq);
@@ -347,7 +347,7 @@ extern "C" pa_status pa_seq_get(const pa_allocator* a, int32_t seq, int32_t* blo
 }
 
 extern "C" pa_status pa_export_tables(const pa_allocator* a, const int32_t* seqs, int32_t n,
-                                      int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out) {
+                                      int32_t max_blocks_per_seq, int32_t* tables_out, int32_t* context_lens_out) noexcept {
   if (!a || n < 0 || max_blocks_per_seq < 0 || (n > 0 && (!seqs || !tables_out || !context_lens_out)))
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_export_tables: bad argument");
   for (int32_t i = 0; i < n; ++i) {
@@ -368,12 +368,12 @@ extern "C" pa_status pa_export_tables(const pa_allocator* a, const int32_t* seqs
   return ok();
 }
 
-extern "C" int32_t pa_block_refcount(const pa_allocator* a, int32_t block) {
+extern "C" int32_t pa_block_refcount(const pa_allocator* a, int32_t block) noexcept {
   if (!a || block < 0 || block >= a->num_blocks) return -1;
   return a->refcount[block];
 }
 
-extern "C" pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out) {
+extern "C" pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_stats* out) noexcept {
   if (!a || !out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_get_stats: NULL argument");
   out->num_blocks = a->num_blocks;
   out->num_free = a->nfree;
@@ -396,7 +396,7 @@ extern "C" pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_
   return ok();
 }
 
-extern "C" int32_t pa_latest_arrival(const pa_allocator* a) {
+extern "C" int32_t pa_latest_arrival(const pa_allocator* a) noexcept {
   if (!a) return -1;
   for (auto it = a->arrival.rbegin(); it != a->arrival.rend(); ++it)
     if (a->seqs.count(*it)) return *it;

@@ -72,7 +72,7 @@ void timing_release() {
 
 extern "C" pa_status pa_kv_append(const pa_kv_cache* cache, const void* k_new, const void* v_new, int32_t act,
                                   const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
-                                  int32_t max_blocks_per_seq, void* stream) {
+                                  int32_t max_blocks_per_seq, void* stream) noexcept {
   static const char* fn = "pa_kv_append";
   if (pa_status s = check_cache(cache, fn)) return s;
   if (pa_status s = check_act(cache, act, fn)) return s;
@@ -87,7 +87,7 @@ extern "C" pa_status pa_kv_append(const pa_kv_cache* cache, const void* k_new, c
 extern "C" pa_status pa_kv_write_prompt(const pa_kv_cache* cache, const void* k_src, const void* v_src, int32_t act,
                                         const int64_t* src_row, const int32_t* start_pos, const int32_t* count,
                                         const int32_t* block_tables, int32_t num_seqs, int32_t max_blocks_per_seq,
-                                        int32_t max_count, void* stream) {
+                                        int32_t max_count, void* stream) noexcept {
   static const char* fn = "pa_kv_write_prompt";
   if (pa_status s = check_cache(cache, fn)) return s;
   if (pa_status s = check_act(cache, act, fn)) return s;
@@ -103,7 +103,7 @@ extern "C" pa_status pa_kv_write_prompt(const pa_kv_cache* cache, const void* k_
 }
 
 extern "C" pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src_dst_pairs, int32_t n,
-                                    void* stream) {
+                                    void* stream) noexcept {
   static const char* fn = "pa_copy_blocks";
   if (pa_status s = check_cache(cache, fn)) return s;
   if (n < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: negative pair count", fn);
@@ -113,7 +113,7 @@ extern "C" pa_status pa_copy_blocks(const pa_kv_cache* cache, const int32_t* src
 }
 
 extern "C" pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, const int32_t* block_ids,
-                                    int32_t n, int32_t direction, void* stream) {
+                                    int32_t n, int32_t direction, void* stream) noexcept {
   static const char* fn = "pa_swap_blocks";
   if (pa_status s = check_cache(cache, fn)) return s;
   if (n < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: negative block count", fn);
@@ -156,12 +156,12 @@ static int32_t shared_parts_for(int32_t max_context_len, int32_t max_shared_toke
 }
 
 extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                           int32_t max_context_len) {
+                                           int32_t max_context_len) noexcept {
   return workspace_bytes_for(num_seqs, num_q_heads, head_dim, max_parts_for(max_context_len));
 }
 
 extern "C" size_t pa_decode_shared_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                                  int32_t max_context_len, int32_t max_shared_tokens) {
+                                                  int32_t max_context_len, int32_t max_shared_tokens) noexcept {
   return workspace_bytes_for(num_seqs, num_q_heads, head_dim, shared_parts_for(max_context_len, max_shared_tokens));
 }
 
@@ -306,7 +306,7 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
 extern "C" pa_status pa_decode(const pa_kv_cache* cache, const void* q, void* out, int32_t act, int32_t num_q_heads,
                                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                                int32_t max_blocks_per_seq, int32_t max_context_len, float sm_scale, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               size_t workspace_bytes, void* stream) noexcept {
   return decode_common("pa_decode", cache, q, nullptr, nullptr, out, act, num_q_heads, block_tables, context_lens,
                        num_seqs, max_blocks_per_seq, max_context_len, sm_scale, workspace, workspace_bytes, stream);
 }
@@ -315,7 +315,7 @@ extern "C" pa_status pa_decode_step(const pa_kv_cache* cache, const void* q, con
                                     void* out, int32_t act, int32_t num_q_heads, const int32_t* block_tables,
                                     const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                                     int32_t max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+                                    void* stream) noexcept {
   if (num_seqs > 0 && (!k_new || !v_new))
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_decode_step: k_new/v_new is NULL");
   return decode_common("pa_decode_step", cache, q, k_new, v_new, out, act, num_q_heads, block_tables, context_lens,
@@ -328,13 +328,13 @@ extern "C" pa_status pa_decode_shared_prefix(const pa_kv_cache* cache, const voi
                                              int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len,
                                              float sm_scale, int32_t num_groups, const int32_t* group_start,
                                              const int32_t* group_shared_blocks, void* workspace,
-                                             size_t workspace_bytes, void* stream) {
+                                             size_t workspace_bytes, void* stream) noexcept {
   return decode_common("pa_decode_shared_prefix", cache, q, k_new, v_new, out, act, num_q_heads, block_tables,
                        context_lens, num_seqs, max_blocks_per_seq, max_context_len, sm_scale, workspace,
                        workspace_bytes, stream, num_groups, group_start, group_shared_blocks);
 }
 
-extern "C" pa_status pa_timing_enable(int32_t on) {
+extern "C" pa_status pa_timing_enable(int32_t on) noexcept {
   timing_release();
   if (!on) return ok();
   g_timing.part_ev.resize(2 * kTimingSlots);
@@ -353,7 +353,7 @@ extern "C" pa_status pa_timing_enable(int32_t on) {
   return ok();
 }
 
-extern "C" pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches) {
+extern "C" pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches) noexcept {
   if (!decode_ms || !decode_launches) return fail(PA_ERR_INVALID_ARGUMENT, "pa_timing_read: NULL argument");
   *decode_ms = 0.0;
   *decode_launches = g_timing.n_part;

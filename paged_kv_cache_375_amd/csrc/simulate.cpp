@@ -33,7 +33,7 @@ struct AllocatorGuard {
 
 extern "C" pa_status pa_simulate_arrivals(int32_t num_blocks, int32_t block_size, const int32_t* arrivals,
                                           const int32_t* lengths, int32_t n, pa_arrival_readout* out,
-                                          int32_t* trace, int32_t trace_cap) {
+                                          int32_t* trace, int32_t trace_cap) noexcept {
   static const char* fn = "pa_simulate_arrivals";
   if (!out || n < 0 || num_blocks < 0 || block_size < 1 || trace_cap < 0 || (trace_cap > 0 && !trace) ||
       (n > 0 && (!arrivals || !lengths)))

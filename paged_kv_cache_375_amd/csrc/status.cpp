@@ -24,7 +24,7 @@ pa_status ok() {
 
 }  // namespace pa
 
-extern "C" const char* pa_status_str(pa_status s) {
+extern "C" const char* pa_status_str(pa_status s) noexcept {
   switch (s) {
     case PA_OK: return "PA_OK";
     case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
@@ -37,4 +37,4 @@ extern "C" const char* pa_status_str(pa_status s) {
   return "PA_ERR_UNKNOWN_STATUS";
 }
 
-extern "C" const char* pa_last_error(void) { return g_last_error; }
+extern "C" const char* pa_last_error(void) noexcept { return g_last_error; }
