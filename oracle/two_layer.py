@@ -1,146 +1,154 @@
 """The two-layer cached-vs-recomputed model — TEST INFRASTRUCTURE ONLY.
 
-The "KV 缓存" topic page (aiinfact.com), level-3 script, runs one small model
-two ways and requires the same result:
-  * recompute: every step runs the whole prefix through every layer, and a
-    layer finishes all positions before the next layer starts (position i
-    attends over positions 0..i);
-  * cached: every step projects only the new position's K and V, appends them
-    to the layer's cache, and attends over the cache.
-Layers have square q/k/v projections only; a layer's output at a position is
-its attention output, which feeds the next layer.  The page warns that a
-version updating only the last position per layer passed with one layer and
-diverged with two, so the model here has two layers.
+The "KV 缓存" topic page (aiinfact.com), level-3 script, describes one small
+attention model (two layers of width 32, 40 positions) computed two ways that
+must agree:
 
-Here the cached path keeps each layer's K/V in a paged pool (block size 4,
-shuffled physical placement) and reads it through the C oracle's append and
-paged decode, so the equivalence ties the paged decode to the recomputed
-contiguous attention.
+  * without a cache, producing position n means running the whole prefix
+    0..n through both layers again; inside a layer every position is brought
+    up to date before the next layer begins, and position i only looks at
+    positions 0..i;
+  * with a cache, only the newest position's K and V are projected in each
+    layer and added to that layer's store; the query of the new position then
+    attends over everything the store holds.
 
-Multiply-accumulates are counted where they happen: one per multiply-add in
-the projection loops, in the recomputed attention loops, and (returned by the
-C oracle) in the paged decode's two dot-product loops.  Account A counts the
-K and V projections only; account B counts the q/k/v projections plus the
-score and weighted-sum loops [AIF level-2 knob, level-3 account table].
+A layer has square query, key and value projections and nothing else; what it
+hands to the next layer at a position is its attention output there.  The
+page retracted an earlier version whose uncached path refreshed only the last
+position per layer: with one layer it agreed, with two it did not.
+
+Written here in matrix form.  The uncached path of one layer is
+
+    Q = X Wq^T,  K = X Wk^T,  V = X Wv^T          (X: [n][D], one row per position)
+    S = (Q K^T) / sqrt(D),  S[i][j] = -inf for j > i   (the causal mask)
+    Y = softmax_rows(S) V                          (max-subtracted, float64)
+
+and Y becomes the next layer's X.  The cached path keeps each layer's K and V
+in a paged pool (block size 4, shuffled physical placement) written by the C
+oracle's append and read by its paged decode, so the agreement of the two
+paths also ties the paged decode to plain causal attention.
+
+Multiply-accumulates are counted as the page's two accounts do
+[AIF level-2 knob, level-3 account table]: account A is the K and V
+projections; account B adds the Q projection, the scores and the weighted
+sums.  A product of an [n][D] matrix by a [D][D] one is n * D * D of them;
+causal attention costs D for the score and D for the weighted sum of every
+(query, key) pair the mask lets through; the paged decode reports its own
+count.  Softmax, scaling and the mask itself are not counted.
 """
-import math
-
 import numpy as np
 
-from . import F64, append as paged_append, decode as paged_decode
+from . import append as paged_append, decode as paged_decode
 from .allocator import OracleAllocator
 
 
-class Counter:
+class MacCount:
+    """Multiply-accumulates per kind: projections (q, k, v) and attention."""
+
     def __init__(self):
-        self.q = self.k = self.v = self.attn = 0
+        self.proj = {"q": 0, "k": 0, "v": 0}
+        self.attention = 0
 
     @property
     def account_a(self):
-        return self.k + self.v
+        return self.proj["k"] + self.proj["v"]
 
     @property
     def account_b(self):
-        return self.q + self.k + self.v + self.attn
+        return sum(self.proj.values()) + self.attention
 
 
-def matvec(W, x, counter=None, kind=None):
-    out = []
-    for row in W:
-        acc = 0.0
-        for a, b in zip(row, x):
-            acc += a * b
-        out.append(acc)
-    if counter is not None:
-        setattr(counter, kind, getattr(counter, kind) + len(W) * len(x))
-    return out
+def project(W, X, count=None, kind=None):
+    """Rows of X mapped by W: X W^T, float64."""
+    W = np.asarray(W, dtype=np.float64)
+    X = np.atleast_2d(np.asarray(X, dtype=np.float64))
+    if count is not None:
+        count.proj[kind] += X.shape[0] * W.shape[0] * W.shape[1]
+    return X @ W.T
 
 
-def attend(q, keys, values, scale, counter=None):
-    scores = []
-    for k in keys:
-        acc = 0.0
-        for a, b in zip(q, k):
-            acc += a * b
-        scores.append(scale * acc)
-    m = max(scores)
-    w = [math.exp(s - m) for s in scores]
-    z = sum(w)
-    out = [0.0] * len(values[0])
-    for t, v in enumerate(values):
-        for i, vi in enumerate(v):
-            out[i] += w[t] * vi
-    if counter is not None:
-        counter.attn += len(keys) * len(q) + len(values) * len(values[0])
-    return [o / z for o in out]
+def causal_attention(Q, K, V, first_pos=0, count=None):
+    """Scaled dot-product attention of query rows at positions first_pos,
+    first_pos + 1, ... over key/value rows 0..len(K)-1; the query at
+    position p sees keys 0..p only."""
+    Q, K, V = (np.atleast_2d(np.asarray(a, dtype=np.float64)) for a in (Q, K, V))
+    dim = Q.shape[1]
+    pos = first_pos + np.arange(Q.shape[0])[:, None]
+    allowed = np.arange(K.shape[0])[None, :] <= pos
+    S = np.where(allowed, (Q @ K.T) / np.sqrt(dim), -np.inf)
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    if count is not None:
+        count.attention += int(allowed.sum()) * dim * 2
+    return P @ V
 
 
-def forward_all_layers(weights, tokens, counter=None):
-    """Recompute path: returns per-layer outputs for every position of the prefix."""
-    dim = len(tokens[0])
-    scale = 1.0 / math.sqrt(dim)
-    layer_in = [list(t) for t in tokens]
-    per_layer = []
+def recompute(weights, tokens, count=None):
+    """Uncached path: the outputs of the last layer at every position of the
+    prefix `tokens`, each layer brought fully up to date before the next."""
+    X = np.asarray(tokens, dtype=np.float64)
     for Wq, Wk, Wv in weights:
-        keys = [matvec(Wk, t, counter, "k") for t in layer_in]
-        values = [matvec(Wv, t, counter, "v") for t in layer_in]
-        out = []
-        for i, t in enumerate(layer_in):
-            q = matvec(Wq, t, counter, "q")
-            out.append(attend(q, keys[: i + 1], values[: i + 1], scale, counter))
-        per_layer.append(out)
-        layer_in = out  # the whole layer is done before the next starts
-    return per_layer
+        Q = project(Wq, X, count, "q")
+        K = project(Wk, X, count, "k")
+        V = project(Wv, X, count, "v")
+        X = causal_attention(Q, K, V, 0, count)
+    return X
 
 
-class PagedCache:
-    """One paged pool per layer (float64, block size 4, shuffled placement)."""
+class PagedStores:
+    """One paged K/V pool per layer (float64, 1 head, block size 4), each
+    with its own allocator whose free list is a seeded shuffle, holding one
+    sequence (id 0)."""
 
-    def __init__(self, layers, dim, max_tokens, block_size=4, seed=0):
-        nb = 2 * -(-max_tokens // block_size)
-        order = np.random.Generator(np.random.PCG64(seed)).permutation(nb)
-        self.alloc = [OracleAllocator(nb, block_size, order) for _ in range(layers)]
-        for a in self.alloc:
-            a.allocate(0, 0)
-        self.k = [np.zeros((nb, 1, block_size, dim)) for _ in range(layers)]
-        self.v = [np.zeros((nb, 1, block_size, dim)) for _ in range(layers)]
-        self.max_blocks = -(-max_tokens // block_size)
+    def __init__(self, layers, dim, max_positions, block_size=4, seed=0):
         self.block_size = block_size
+        self.max_blocks = -(-max_positions // block_size)
+        nblocks = 2 * self.max_blocks
+        self.layers = []
+        for _ in range(layers):
+            order = np.random.Generator(np.random.PCG64(seed)).permutation(nblocks)
+            alloc = OracleAllocator(nblocks, block_size, order)
+            alloc.allocate(0, 0)
+            pools = (np.zeros((nblocks, 1, block_size, dim)), np.zeros((nblocks, 1, block_size, dim)))
+            self.layers.append((alloc, pools))
+
+    def numbers_held(self):
+        """How many numbers the stores hold: a K and a V vector per position per layer."""
+        return sum(alloc.ctx[0] * 2 * pools[0].shape[-1] for alloc, pools in self.layers)
 
 
-def gen_with_cache(weights, new_token, cache: PagedCache, counter=None):
-    """Cached path: one new position through every layer."""
-    dim = len(new_token)
-    scale = 1.0 / math.sqrt(dim)
-    x = list(new_token)
-    for li, (Wq, Wk, Wv) in enumerate(weights):
-        k = matvec(Wk, x, counter, "k")
-        v = matvec(Wv, x, counter, "v")
-        a = cache.alloc[li]
-        a.append_slot(0)
-        tables, ctx = a.export([0], cache.max_blocks)
-        paged_append(cache.k[li], cache.v[li], np.array([[k]]), np.array([[v]]), tables, ctx, cache.block_size)
-        q = matvec(Wq, x, counter, "q")
-        out, macs = paged_decode(cache.k[li], cache.v[li], np.array([[q]], dtype=np.float64), tables, ctx,
-                                 scale, count_macs=True)
-        if counter is not None:
-            counter.attn += macs
-        x = list(out[0, 0])
-    return x
+def cached_step(weights, token, stores: PagedStores, count=None):
+    """Cached path: the newest position through every layer; returns the last
+    layer's output there.  Each layer reserves the slot, stores the new K and
+    V through the block table, then decodes over the whole table."""
+    x = np.asarray(token, dtype=np.float64)[None, :]
+    for (Wq, Wk, Wv), (alloc, (kpool, vpool)) in zip(weights, stores.layers):
+        k_row = project(Wk, x, count, "k")
+        v_row = project(Wv, x, count, "v")
+        alloc.append_slot(0)
+        table, lens = alloc.export([0], stores.max_blocks)
+        paged_append(kpool, vpool, k_row[:, None, :], v_row[:, None, :], table, lens, stores.block_size)
+        q_row = project(Wq, x, count, "q")
+        y, macs = paged_decode(kpool, vpool, q_row[:, None, :], table, lens, 1.0 / np.sqrt(x.shape[1]),
+                               count_macs=True)
+        if count is not None:
+            count.attention += macs
+        x = y[:, 0, :]
+    return x[0]
 
 
 def run_both(tokens, weights):
-    """Returns (max abs difference over every prefix, recompute counter, cached counter, occupancy)."""
-    positions, dim = len(tokens), len(tokens[0])
-    layers = len(weights)
-    rc, cc = Counter(), Counter()
-    cache = PagedCache(layers, dim, positions)
-    worst = 0.0
-    occupancy = []
-    for n in range(1, positions + 1):
-        full = forward_all_layers(weights, tokens[:n], rc)[-1][-1]
-        step = gen_with_cache(weights, tokens[n - 1], cache, cc)
-        worst = max(worst, max(abs(a - b) for a, b in zip(full, step)))
-        # numbers the caches hold: every layer keeps a K and a V vector per position
-        occupancy.append(sum(a.ctx[0] for a in cache.alloc) * 2 * dim)
-    return worst, rc, cc, occupancy
+    """Both paths over every prefix of `tokens`.  Returns (largest absolute
+    difference seen, uncached MAC count, cached MAC count, numbers held by the
+    caches after each position)."""
+    tokens = np.asarray(tokens, dtype=np.float64)
+    weights = np.asarray(weights, dtype=np.float64)
+    uncached, cached = MacCount(), MacCount()
+    stores = PagedStores(len(weights), tokens.shape[1], len(tokens))
+    worst, held = 0.0, []
+    for n in range(1, len(tokens) + 1):
+        want = recompute(weights, tokens[:n], uncached)[-1]
+        got = cached_step(weights, tokens[n - 1], stores, cached)
+        worst = max(worst, float(np.max(np.abs(want - got))))
+        held.append(stores.numbers_held())
+    return worst, uncached, cached, held

@@ -74,7 +74,7 @@ def test_two_layer_cached_equals_recomputed_with_exact_counts():
     g = _golden("two_layer_counts.json")
     c = g["config"]
     tokens, weights = two_layer_inputs(0, c["layers"], c["dim"], c["positions"])
-    worst, rc, cc, occ = two_layer.run_both(tokens.tolist(), weights.tolist())
+    worst, rc, cc, occ = two_layer.run_both(tokens, weights)
     assert worst < 1e-13  # the page saw 6.7e-16 between its two float64 paths
     assert rc.account_b == g["account_b_macs"]["uncached"]
     assert cc.account_b == g["account_b_macs"]["cached"]
@@ -87,27 +87,24 @@ def test_two_layer_cached_equals_recomputed_with_exact_counts():
 
 
 def test_two_layer_single_layer_bug_would_be_caught():
-    """A recompute path that updates only the last position per layer (the bug
-    the page retracted) agrees with one layer and diverges with two."""
+    """An uncached path that refreshes only the last position per layer (the
+    bug the page retracted) agrees with one layer and diverges with two."""
     tokens, weights = two_layer_inputs(0, 2, 8, 6)
-    tokens, weights = tokens.tolist(), weights.tolist()
 
-    def buggy(ws, toks):
-        layer_in = [list(t) for t in toks]
+    def stale_history(ws, toks):
+        X = np.array(toks, dtype=np.float64)
         for Wq, Wk, Wv in ws:
-            keys = [two_layer.matvec(Wk, t) for t in layer_in]
-            values = [two_layer.matvec(Wv, t) for t in layer_in]
-            q = two_layer.matvec(Wq, layer_in[-1])
-            last = two_layer.attend(q, keys, values, 1 / math.sqrt(len(q)))
-            layer_in = layer_in[:-1] + [last]  # history keeps the raw input
-        return layer_in[-1]
+            K, V = two_layer.project(Wk, X), two_layer.project(Wv, X)
+            last = two_layer.causal_attention(two_layer.project(Wq, X[-1:]), K, V, len(X) - 1)
+            X = np.concatenate([X[:-1], last])  # earlier rows keep the layer's input
+        return X[-1]
 
     for layers, should_agree in ((1, True), (2, False)):
         ws = weights[:layers]
-        cache = two_layer.PagedCache(layers, 8, 6)
+        stores = two_layer.PagedStores(layers, 8, 6)
         diff = 0.0
         for n in range(1, 7):
-            a = buggy(ws, tokens[:n])
-            b = two_layer.gen_with_cache(ws, tokens[n - 1], cache)
-            diff = max(diff, max(abs(x - y) for x, y in zip(a, b)))
+            a = stale_history(ws, tokens[:n])
+            b = two_layer.cached_step(ws, tokens[n - 1], stores)
+            diff = max(diff, float(np.max(np.abs(a - b))))
         assert (diff < 1e-12) == should_agree, (layers, diff)
