@@ -77,73 +77,64 @@ def measured_traffic(workload, launch_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
-def oracle_decode_threaded(ref, threads):
-    """The CPU reference's decode of every (sequence, head), spread over
-    `threads` host threads: each thread decodes its own share of the pairs
-    with the unchanged reference routine (a C call, which runs without the
-    interpreter lock).  Shares are dealt longest context first.  Returns
-    [num_seqs][hq][d] float64, the same values as ref.decode()."""
+def cpu_baseline(dr, warmup=2, samples=10):
+    """The CPU reference (plain scalar C, fp64) on the same step, by the
+    timing method of the "KV 缓存" topic page's level-3 script: inputs built
+    outside the timed region, `warmup` untimed runs, then `samples` timed
+    runs reported as median [min, max].  The reported value spreads the
+    decode's (sequence, head) pairs over the host's threads; the
+    single-thread figure times a bounded sample of those pairs (every pair
+    costs in proportion to its context) and scales it to the whole step."""
     import numpy as np
-    from concurrent.futures import ThreadPoolExecutor
 
-    B, hq, d = ref.dr.q.shape
-    ctx = np.asarray(ref.sc.ctx)
-    pairs = sorted(((s, h) for s in range(B) for h in range(hq)), key=lambda p: (-int(ctx[p[0]]), p))
-    shares = [pairs[i::threads] for i in range(threads)]
-    out = np.zeros((B, hq, d), dtype=np.float64)
-
-    def work(share):
-        if share:
-            seqs, heads = zip(*share)
-            out[list(seqs), list(heads)] = ref.decode_pairs(list(seqs), list(heads))
-
-    with ThreadPoolExecutor(threads) as ex:
-        list(ex.map(work, shares))
-    return out
-
-
-def host_threads():
-    """Host threads the CPU baseline uses: the CPUs this process may run on,
-    at most 16."""
-    try:
-        n = len(os.sched_getaffinity(0))
-    except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
-
-
-def cpu_baseline(dr, repeats):
-    """The CPU reference (plain scalar C, fp64) on the same step: once on one
-    thread, and once with the decode's (sequence, head) pairs spread over the
-    host's threads (the reported value)."""
     from oracle.allocator import OracleAllocator
-    from oracle.reference_step import ReferenceStep
+    from oracle.reference_step import ReferenceStep, host_threads
     from paged_kv_cache_375_amd.workloads import run_scenario
 
     ref = ReferenceStep(dr, run_scenario(dr, OracleAllocator(dr.num_blocks, dr.wl.block_size, dr.free_order)))
-    times = []
-    for _ in range(repeats):
-        t = time.perf_counter()
-        ref.append()
-        ref.decode()
-        times.append(time.perf_counter() - t)
-    med = statistics.median(times)
     T = host_threads()
-    ttimes = []
-    for _ in range(repeats):
-        t = time.perf_counter()
-        ref.append()
-        oracle_decode_threaded(ref, T)
-        ttimes.append(time.perf_counter() - t)
-    tmed = statistics.median(ttimes)
-    step = f"the whole step (append + decode of all {dr.wl.batch} sequences, every head)"
-    return {"value": dr.wl.batch / tmed, "unit": "tokens/s", "cores": T, "kind": "oracle",
-            "sample": f"{step}, decode pairs spread over {T} threads, {repeats} runs, median {tmed:.3f} s "
-                      f"[min {min(ttimes):.3f}, max {max(ttimes):.3f}]",
-            "single_thread": {"value": dr.wl.batch / med, "unit": "tokens/s", "cores": 1,
-                              "sample": f"{step}, {repeats} runs, median {med:.2f} s "
-                                        f"[min {min(times):.2f}, max {max(times):.2f}]"},
-            "cpu": platform.processor() or platform.machine()}
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ts = []
+        for _ in range(samples):
+            t = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t)
+        return statistics.median(ts), min(ts), max(ts)
+
+    med, lo, hi = timed(lambda: (ref.append(), ref.decode_threaded(T)))
+
+    # single thread: a seeded sample of (sequence, head) pairs holding about
+    # 2.6e7 context elements (~0.5 s here), scaled by the whole step's count
+    B, hq, d = dr.q.shape
+    ctx = np.asarray(ref.sc.ctx, dtype=np.int64)
+    order = np.random.default_rng(0).permutation(B * hq)
+    cum = np.cumsum(ctx[order // hq] * d)
+    n = int(min(len(order), np.searchsorted(cum, 2.6e7) + 1))
+    seqs, heads = (order[:n] // hq).tolist(), (order[:n] % hq).tolist()
+    frac = float(cum[n - 1]) / float(cum[-1])
+    smed, slo, shi = timed(lambda: ref.decode_pairs(seqs, heads))
+    step = f"the whole step (append + decode of all {B} sequences, every head)"
+    how = f"warm-up {warmup}, {samples} timed runs, median [min, max]"
+    return {"value": B / med, "unit": "tokens/s", "cores": T, "kind": "oracle",
+            "sample": f"{step}, decode pairs spread over {T} threads; {how}: {med:.3f} s [{lo:.3f}, {hi:.3f}]",
+            "single_thread": {"value": B * frac / smed, "unit": "tokens/s", "cores": 1,
+                              "sample": f"decode of {n} of {B * hq} (sequence, head) pairs ({frac:.1%} of the "
+                                        f"step's context elements) on one thread, scaled to the whole step; "
+                                        f"{how}: {smed:.3f} s [{slo:.3f}, {shi:.3f}]"},
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def _time_ms(fn, reps):
@@ -255,7 +246,8 @@ def main():
     ap.add_argument("--block-size", type=int, default=0, help="override the workload's block size")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=0, help="pool copies to rotate over (0: enough for >= 2 GB)")
-    ap.add_argument("--cpu-repeats", type=int, default=4, help="CPU reference runs (0 skips the CPU baseline)")
+    ap.add_argument("--cpu-samples", type=int, default=10,
+                    help="timed CPU reference runs after two warm-up runs (0 skips the CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters) and exit")
     ap.add_argument("--writers", action="store_true",
@@ -411,9 +403,9 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes},
     }
-    if args.cpu_repeats > 0:
+    if args.cpu_samples > 0:
         print("bench: timing the CPU reference", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(dr, args.cpu_repeats)
+        result["cpu_baseline"] = cpu_baseline(dr, samples=args.cpu_samples)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result))

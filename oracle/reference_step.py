@@ -5,6 +5,8 @@ for it (both passed in; this module imports nothing from the product), builds
 the pool with the oracle's own prompt write, copy and append, and decodes.
 """
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -47,3 +49,34 @@ class ReferenceStep:
         dr = self.dr
         return decode_pairs(self.k, self.v, dr.q, self.sc.tables, self.sc.ctx, self.sm_scale, seqs, heads,
                             dr.k_scale, dr.v_scale)
+
+    def decode_threaded(self, threads=None):
+        """decode() with the (sequence, head) pairs spread over host threads:
+        each thread runs the unchanged decode_pairs routine (a C call, which
+        runs without the interpreter lock) on its own share, dealt longest
+        context first.  Returns the same values as decode()."""
+        threads = threads or host_threads()
+        B, hq, d = self.dr.q.shape
+        ctx = np.asarray(self.sc.ctx)
+        pairs = sorted(((s, h) for s in range(B) for h in range(hq)), key=lambda p: (-int(ctx[p[0]]), p))
+        shares = [pairs[i::threads] for i in range(threads)]
+        out = np.zeros((B, hq, d), dtype=np.float64)
+
+        def work(share):
+            if share:
+                seqs, heads = zip(*share)
+                out[list(seqs), list(heads)] = self.decode_pairs(list(seqs), list(heads))
+
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, shares))
+        return out
+
+
+def host_threads():
+    """Host threads to spread the reference over: the CPUs this process may
+    run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))

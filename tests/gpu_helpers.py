@@ -1,5 +1,7 @@
 """Shared helpers of the GPU parity tests: build the same workload draw on the
 HIP path and on the CPU reference, each with its own allocator."""
+from dataclasses import replace
+
 import numpy as np
 import torch
 
@@ -44,3 +46,31 @@ def pool_bytes(t):
 def out_f64(t):
     torch.cuda.synchronize()
     return t.float().cpu().numpy().astype(np.float64)
+
+
+def unquantised_reference(dr, scenario):
+    """The reference over an f16 pool holding the same K/V values an FP8
+    workload quantises (same draw, same tables): the unquantised result the
+    FP8 error is reported against."""
+    wl16 = replace(dr.wl, kv="f16", name=dr.wl.name + "_unquantised")
+    dr16 = draw(wl16, 0)
+    assert np.array_equal(dr16.k_hist, dr.k_hist) and np.array_equal(dr16.q, dr.q)
+    ref16 = ReferenceStep(dr16, scenario)
+    ref16.append()
+    return ref16
+
+
+def full_size_check(name, wl, out, ref, dr):
+    """Every output element of a full-size step against the reference (decode
+    spread over host threads), at the bound of the pool dtype; FP8 pools also
+    report their error against the unquantised f16 result."""
+    print(f"[full] {name}: reference decode of {out.shape[0] * out.shape[1]} (sequence, head) outputs", flush=True)
+    want = ref.decode_threaded()
+    err = float(np.max(np.abs(out - want)))
+    print(f"[full] {name}: every output, max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    if wl.kv == "e4m3":
+        unq = unquantised_reference(dr, ref.sc).decode_threaded()
+        print(f"[full] {name}: informational, FP8 against unquantised f16: GPU {np.max(np.abs(out - unq)):.3e}, "
+              f"reference {np.max(np.abs(want - unq)):.3e}", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]

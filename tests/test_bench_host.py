@@ -1,6 +1,7 @@
-"""Host-side parts of the benchmark (no GPU): the threaded CPU baseline
-computes exactly what the reference's single call does, and the one-GPU
-contract is enforced."""
+"""Host-side parts of the benchmark (no GPU): the threaded CPU reference
+(used by the full-size parity tests and the CPU baseline) computes exactly
+what the reference's single call does, the CPU baseline runs, and the
+one-GPU contract is enforced."""
 import subprocess
 import sys
 
@@ -25,7 +26,15 @@ def test_threaded_oracle_decode_equals_single_call():
         ref.append()
         want = ref.decode()
         for threads in (1, 3, 8):
-            assert np.array_equal(bench.oracle_decode_threaded(ref, threads), want)
+            assert np.array_equal(ref.decode_threaded(threads), want)
+
+
+def test_cpu_baseline_record():
+    dr = draw(WORKLOADS["opt13b"].scaled(batch=3, ctx_lo=10, ctx_hi=200), 0)
+    rec = bench.cpu_baseline(dr, warmup=1, samples=2)
+    assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s" and rec["value"] > 0
+    assert rec["cores"] >= 1 and rec["single_thread"]["cores"] == 1 and rec["single_thread"]["value"] > 0
+    assert "median" in rec["sample"]
 
 
 def test_bench_refuses_more_than_one_gpu():

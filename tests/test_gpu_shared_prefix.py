@@ -17,7 +17,7 @@ import torch
 
 from paged_kv_cache_375_amd import api
 from paged_kv_cache_375_amd.workloads import WORKLOADS, Workload
-from tests.gpu_helpers import TOL, build_pair, out_f64, pool_bytes
+from tests.gpu_helpers import TOL, build_pair, full_size_check, out_f64, pool_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -94,9 +94,11 @@ def test_shared_prefix_claim_past_a_context_gives_nan_for_that_sequence_only():
     assert float(np.max(np.abs(out[1:] - want[1:]))) <= TOL["f16"]
 
 
-def test_full_prefix_workload_sampled_parity():
+def test_full_prefix_workload_parity():
     """The FP8 prefix workload at its real size, in the launch the benchmark
-    times for it (shared prefix, append fused)."""
+    times for it (shared prefix, append fused): pool bit-exact, every output
+    element within the bound; the error against the unquantised f16 result
+    is printed for information."""
     wl = WORKLOADS["opt13b_fp8_prefix"]
     print(f"[shared-prefix] {wl.name}: building", flush=True)
     dr, gpu, ref = build_pair(wl)
@@ -104,12 +106,4 @@ def test_full_prefix_workload_sampled_parity():
     ref.append()
     assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
     assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
-    rng = np.random.default_rng(12)
-    B, hq = wl.batch, wl.num_q_heads
-    longest, shortest = int(np.argmax(dr.ctx)), int(np.argmin(dr.ctx))
-    seqs = [longest] * hq + [shortest] * hq + rng.integers(0, B, 64).tolist()
-    heads = list(range(hq)) * 2 + rng.integers(0, hq, 64).tolist()
-    err = float(np.max(np.abs(out[np.array(seqs), np.array(heads)] - ref.decode_pairs(seqs, heads))))
-    print(f"[shared-prefix] {wl.name}: {len(seqs)} sampled outputs, max abs err {err:.3e}", flush=True)
-    assert np.all(np.isfinite(out))
-    assert err <= TOL["e4m3"]
+    full_size_check(wl.name + " (shared-prefix path)", wl, out, ref, dr)

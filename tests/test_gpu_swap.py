@@ -1,89 +1,136 @@
-"""Preemption by swapping on the GPU (needs an MI355X).
+"""Preemption by swapping on the GPU against the CPU reference (needs an
+MI355X).
 
 When blocks run out, the latest arrival gives up all of its blocks and its
 K/V move to host memory; when it resumes, it takes fresh blocks and the K/V
-move back [F55 §放不下的时候].  A correct round trip is invisible to
-attention: the resumed sequence's output must be bit-identical to the one
-before preemption, even though a sequence that ran in between reused (and
-overwrote) the very blocks it gave up.  The host copy must hold each block's
-bytes exactly.
+move back [F55 §放不下的时候].  The reference replays the same trace on its
+own allocator model and its own pools: the prompts are written with its
+prompt write, its host copy is the pool's blocks as they were at swap-out,
+and the swap-in copies them back into the fresh blocks.  The GPU's host copy
+and its pool after swap-in must equal the reference's bytes exactly, even
+though a sequence that ran in between reused (and overwrote) the very blocks
+the victim gave up; the resumed decode must meet the bound against the
+reference's decode and be bit-identical to the GPU's decode before
+preemption.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
+from oracle.allocator import OracleAllocator
 from paged_kv_cache_375_amd import api
-from tests.gpu_helpers import pool_bytes
+from tests.gpu_helpers import TOL, out_f64, pool_bytes
 
 pytestmark = pytest.mark.gpu
 
 # (pool dtype, block size, KV heads, head_dim)
 CASES = [("f16", 16, 8, 128), ("f32", 4, 2, 64), ("e4m3", 1, 4, 32), ("e4m3", 16, 1, 128)]
+NP_POOL = {"f16": np.float16, "f32": np.float32, "e4m3": np.uint8}
+SCALES = dict(k_scale=0.05, v_scale=0.04, k_inv_scale=20.0, v_inv_scale=25.0)
 
 
-def _prompt(cache, alloc, seq, rows, act, max_blocks, gen):
-    """Write a random prompt of `rows` tokens for seq into its blocks."""
-    k = torch.randn(rows, cache.num_kv_heads, cache.head_dim, generator=gen).to(act).cuda()
-    v = torch.randn(rows, cache.num_kv_heads, cache.head_dim, generator=gen).to(act).cuda()
-    tables, _ = alloc.export([seq], max_blocks)
-    i64 = lambda x: torch.tensor([x], dtype=torch.int64).cuda()
-    i32 = lambda x: torch.tensor([x], dtype=torch.int32).cuda()
-    api.kv_write_prompt(cache, k, v, i64(0), i32(0), i32(rows), torch.from_numpy(tables).cuda(), rows)
+class Both:
+    """The library's allocator and pool beside the reference's, driven by the
+    same calls; every table is checked to agree."""
 
+    def __init__(self, kv, bs, hkv, d, nb, free_order):
+        self.kv, self.bs, self.hkv, self.d = kv, bs, hkv, d
+        self.scales = SCALES if kv == "e4m3" else dict(k_scale=1.0, v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0)
+        self.alloc = api.Allocator(nb, bs, free_order)
+        self.ralloc = OracleAllocator(nb, bs, free_order)
+        self.cache = api.KVCache(nb, bs, hkv, d, kv, "cuda", **self.scales)
+        self.rk = np.zeros((nb, hkv, bs, d), dtype=NP_POOL[kv])
+        self.rv = np.zeros_like(self.rk)
 
-def _decode(cache, alloc, q, seqs, max_blocks, max_ctx):
-    tables, ctx = alloc.export(seqs, max_blocks)
-    return api.decode(cache, q, torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(), max_ctx,
-                      q.shape[-1] ** -0.5).clone()
+    def call(self, name, *args):
+        a, b = getattr(self.alloc, name)(*args), getattr(self.ralloc, name)(*args)
+        if a is not None or b is not None:
+            assert list(a) == list(b), (name, a, b)
+        return a
+
+    def tables(self, seqs, max_blocks):
+        t, c = self.alloc.export(seqs, max_blocks)
+        rt, rc = self.ralloc.export(seqs, max_blocks)
+        assert np.array_equal(t, rt) and np.array_equal(c, rc)
+        return t, c
+
+    def write_prompt(self, seq, k, v):
+        """Prompt rows k, v ([rows][hkv][d], activation dtype) of seq into its blocks, on both sides."""
+        rows = k.shape[0]
+        tables, _ = self.tables([seq], -(-rows // self.bs))
+        i64 = lambda x: torch.tensor([x], dtype=torch.int64).cuda()
+        i32 = lambda x: torch.tensor([x], dtype=torch.int32).cuda()
+        api.kv_write_prompt(self.cache, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), i64(0), i32(0),
+                            i32(rows), torch.from_numpy(tables).cuda(), rows)
+        oracle.write_tokens(self.rk, self.rv, k, v, [0], [0], [rows], tables, self.scales["k_inv_scale"],
+                            self.scales["v_inv_scale"])
+
+    def decode(self, q, seqs, max_blocks, max_ctx):
+        tables, ctx = self.tables(seqs, max_blocks)
+        sm_scale = float(np.float32(q.shape[-1] ** -0.5))
+        got = api.decode(self.cache, torch.from_numpy(q).cuda(), torch.from_numpy(tables).cuda(),
+                         torch.from_numpy(ctx).cuda(), max_ctx, sm_scale).clone()
+        want = oracle.decode(self.rk, self.rv, q, tables, ctx, sm_scale, self.scales["k_scale"],
+                             self.scales["v_scale"])
+        return got, want
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "{}_bs{}_kv{}_d{}".format(*c))
-def test_swap_round_trip_bit_exact_and_decode_unchanged(case):
+def test_swap_round_trip_matches_reference(case):
     kv, bs, hkv, d = case
     print(f"[swap] {case}", flush=True)
-    act = torch.float32 if kv == "f32" else torch.float16
-    gen = torch.Generator().manual_seed(100 + CASES.index(case))
+    act = np.float32 if kv == "f32" else np.float16
+    rng = np.random.default_rng(100 + CASES.index(case))
+    normal = lambda *shape: rng.standard_normal(shape, dtype=np.float32).astype(act)
     lens = [700, 333]                      # sequence 1 arrives last
     need = [-(-n // bs) for n in lens]
     nb = sum(need) + 1                     # tight: whoever runs next must reuse sequence 1's blocks
     max_blocks, max_ctx = max(need), max(lens)
-    alloc = api.Allocator(nb, bs, np.random.default_rng(1).permutation(nb))
-    scale = dict(k_scale=0.05, v_scale=0.04, k_inv_scale=20.0, v_inv_scale=25.0) if kv == "e4m3" else {}
-    cache = api.KVCache(nb, bs, hkv, d, kv, "cuda", **scale)
+    both = Both(kv, bs, hkv, d, nb, np.random.default_rng(1).permutation(nb))
     for s, n in enumerate(lens):
-        alloc.allocate(s, n)
-        _prompt(cache, alloc, s, n, act, max_blocks, gen)
-    q = torch.randn(2, 2 * hkv, d, generator=gen).to(act).cuda()
-    before = _decode(cache, alloc, q, [0, 1], max_blocks, max_ctx)
+        both.call("allocate", s, n)
+        both.write_prompt(s, normal(n, hkv, d), normal(n, hkv, d))
+    q = normal(2, 2 * hkv, d)
+    before, want_before = both.decode(q, [0, 1], max_blocks, max_ctx)
+    assert float(np.max(np.abs(out_f64(before) - want_before))) <= TOL[kv]
 
-    victim = alloc.latest_arrival()
-    assert victim == 1
-    out_ids = alloc.swap_out(victim)
+    victim = both.alloc.latest_arrival()
+    assert victim == 1 == both.ralloc.latest_arrival()
+    out_ids = both.call("swap_out", victim)
     n = len(out_ids)
-    host_k = torch.empty((n, hkv, bs, d), dtype=cache.k.dtype).pin_memory()
-    host_v = torch.empty_like(host_k).pin_memory()
-    api.swap_blocks(cache, host_k, host_v, torch.tensor(out_ids, dtype=torch.int32).cuda(), "out")
-    torch.cuda.synchronize()
     ids = np.array(out_ids)
-    assert np.array_equal(host_k.numpy().view(np.uint8), pool_bytes(cache.k)[ids])
-    assert np.array_equal(host_v.numpy().view(np.uint8), pool_bytes(cache.v)[ids])
+    host_k = torch.empty((n, hkv, bs, d), dtype=both.cache.k.dtype).pin_memory()
+    host_v = torch.empty_like(host_k).pin_memory()
+    api.swap_blocks(both.cache, host_k, host_v, torch.tensor(out_ids, dtype=torch.int32).cuda(), "out")
+    ref_host_k, ref_host_v = both.rk[ids].copy(), both.rv[ids].copy()  # the reference's swap-out
+    torch.cuda.synchronize()
+    assert np.array_equal(host_k.numpy().view(np.uint8), ref_host_k.view(np.uint8))
+    assert np.array_equal(host_v.numpy().view(np.uint8), ref_host_v.view(np.uint8))
 
     # another sequence runs in the freed blocks and overwrites them
-    intruder_len = alloc.num_free() * bs
-    alloc.allocate(2, intruder_len)
-    assert set(out_ids) <= set(alloc.table(2))
-    _prompt(cache, alloc, 2, intruder_len, act, -(-intruder_len // bs), gen)
+    intruder_len = both.alloc.num_free() * bs
+    both.call("allocate", 2, intruder_len)
+    assert set(out_ids) <= set(both.alloc.table(2))
+    both.write_prompt(2, normal(intruder_len, hkv, d), normal(intruder_len, hkv, d))
     torch.cuda.synchronize()
-    assert not np.array_equal(pool_bytes(cache.k)[ids], host_k.numpy().view(np.uint8))
-    alloc.free_seq(2)
+    assert not np.array_equal(pool_bytes(both.cache.k)[ids], host_k.numpy().view(np.uint8))
+    both.call("free_seq", 2)
 
-    in_ids = alloc.swap_in(victim)
+    in_ids = both.call("swap_in", victim)
     assert len(in_ids) == n and in_ids != out_ids  # fresh blocks, placed elsewhere
-    api.swap_blocks(cache, host_k, host_v, torch.tensor(in_ids, dtype=torch.int32).cuda(), "in")
-    after = _decode(cache, alloc, q, [0, 1], max_blocks, max_ctx)
+    api.swap_blocks(both.cache, host_k, host_v, torch.tensor(in_ids, dtype=torch.int32).cuda(), "in")
+    both.rk[np.array(in_ids)], both.rv[np.array(in_ids)] = ref_host_k, ref_host_v  # the reference's swap-in
+    after, want_after = both.decode(q, [0, 1], max_blocks, max_ctx)
     torch.cuda.synchronize()
+    live = np.array(both.alloc.table(0) + in_ids)
+    assert np.array_equal(pool_bytes(both.cache.k)[live], both.rk[live].view(np.uint8))
+    assert np.array_equal(pool_bytes(both.cache.v)[live], both.rv[live].view(np.uint8))
+    err = float(np.max(np.abs(out_f64(after) - want_after)))
+    print(f"[swap] {case}: {n} blocks out and back; resumed decode max abs err {err:.3e} (bound {TOL[kv]})",
+          flush=True)
+    assert err <= TOL[kv]
     assert torch.equal(before, after)
-    print(f"[swap] {case}: {n} blocks out and back, decode bit-identical", flush=True)
 
 
 def test_swap_skips_out_of_range_ids():
