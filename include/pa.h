@@ -54,7 +54,9 @@
 #include <stdint.h>
 
 /* Every entry point is noexcept for C++ callers: no exception leaves the
- * library (an allocation failure inside it ends the process). */
+ * library.  A host memory allocation that fails inside a call returns
+ * PA_ERR_HOST_MEMORY, and the call changes nothing (the allocator's state is
+ * as before it). */
 #ifdef __cplusplus
 #define PA_NOEXCEPT noexcept
 #else
@@ -72,7 +74,8 @@ typedef enum {
   PA_ERR_UNKNOWN_SEQ = 3,
   PA_ERR_WORKSPACE_TOO_SMALL = 4,
   PA_ERR_UNSUPPORTED = 5,
-  PA_ERR_HIP = 6
+  PA_ERR_HIP = 6,
+  PA_ERR_HOST_MEMORY = 7
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARGUMENT, PA_ERR_OUT_OF_BLOCKS, PA_ERR_UNKNOWN_SEQ = 0, 1, 2, 3
-PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 4, 5, 6
+PA_ERR_WORKSPACE_TOO_SMALL, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_HOST_MEMORY = 4, 5, 6, 7
 PA_F32, PA_F16, PA_FP8_E4M3 = 0, 1, 2
 PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 

@@ -24,8 +24,10 @@
 // The free list is first in, first out (least recently freed goes first);
 // blocks freed together join its tail in logical order.  It is an intrusive
 // doubly linked list, so a cached block is claimed back from the middle in
-// O(1).  Every operation validates before it mutates, so a failing call
-// leaves the state unchanged.
+// O(1).  Every operation validates before it mutates, and makes every host
+// allocation it needs (vector room, map nodes) before the first change, so a
+// failing call, a failed host allocation included, leaves the state
+// unchanged; no exception leaves an entry point (PA_ERR_HOST_MEMORY).
 #include <algorithm>
 #include <cstring>
 #include <new>
@@ -112,6 +114,17 @@ uint64_t block_key(uint64_t parent, const int32_t* tokens, int32_t bs) {
 using pa::fail;
 using pa::ok;
 
+// The body of an entry point, with a failed host allocation (the only
+// exception the standard containers used here throw) turned into a status.
+#define PA_GUARDED(fn, ...)                                                   \
+  try {                                                                       \
+    __VA_ARGS__                                                               \
+  } catch (const std::bad_alloc&) {                                           \
+    return fail(PA_ERR_HOST_MEMORY, "%s: out of host memory", fn);            \
+  } catch (...) {                                                             \
+    return fail(PA_ERR_HOST_MEMORY, "%s: unexpected host failure", fn);       \
+  }
+
 extern "C" pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
                                          pa_allocator** out) noexcept {
   if (!out) return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: out is NULL");
@@ -120,26 +133,32 @@ extern "C" pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: num_blocks %d, block_size %d", num_blocks,
                 block_size);
   pa_allocator* a = new (std::nothrow) pa_allocator;
-  if (!a) return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: out of host memory");
-  a->num_blocks = num_blocks;
-  a->block_size = block_size;
-  a->refcount.assign(num_blocks, 0);
-  a->fnext.assign(num_blocks, -1);
-  a->fprev.assign(num_blocks, -1);
-  a->is_free.assign(num_blocks, 0);
-  if (free_order) {
-    std::vector<char> seen(num_blocks, 0);
-    for (int32_t i = 0; i < num_blocks; ++i) {
-      int32_t b = free_order[i];
-      if (b < 0 || b >= num_blocks || seen[b]) {
-        delete a;
-        return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: free_order is not a permutation (entry %d)", i);
+  if (!a) return fail(PA_ERR_HOST_MEMORY, "pa_allocator_create: out of host memory");
+  try {
+    a->num_blocks = num_blocks;
+    a->block_size = block_size;
+    a->refcount.assign(num_blocks, 0);
+    a->fnext.assign(num_blocks, -1);
+    a->fprev.assign(num_blocks, -1);
+    a->is_free.assign(num_blocks, 0);
+    if (free_order) {
+      std::vector<char> seen(num_blocks, 0);
+      for (int32_t i = 0; i < num_blocks; ++i) {
+        int32_t b = free_order[i];
+        if (b < 0 || b >= num_blocks || seen[b]) {
+          delete a;
+          return fail(PA_ERR_INVALID_ARGUMENT, "pa_allocator_create: free_order is not a permutation (entry %d)",
+                      i);
+        }
+        seen[b] = 1;
+        a->push_free(b);
       }
-      seen[b] = 1;
-      a->push_free(b);
+    } else {
+      for (int32_t b = 0; b < num_blocks; ++b) a->push_free(b);
     }
-  } else {
-    for (int32_t b = 0; b < num_blocks; ++b) a->push_free(b);
+  } catch (...) {
+    delete a;
+    return fail(PA_ERR_HOST_MEMORY, "pa_allocator_create: out of host memory for %d blocks", num_blocks);
   }
   *out = a;
   return ok();
@@ -159,13 +178,18 @@ extern "C" pa_status pa_seq_allocate(pa_allocator* a, int32_t seq, int32_t num_t
   if (need > a->nfree)
     return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_allocate: sequence %d needs %lld blocks, %d free", seq,
                 static_cast<long long>(need), a->nfree);
-  pa_allocator::Seq s;
-  s.blocks.reserve(need);
-  for (int64_t i = 0; i < need; ++i) s.blocks.push_back(a->take());
-  s.ctx = num_tokens;
-  a->seqs.emplace(seq, std::move(s));
-  a->arrival.push_back(seq);
-  return ok();
+  PA_GUARDED("pa_seq_allocate", {
+    // every allocation first: the arrival slot, the table, the map node
+    a->arrival.reserve(a->arrival.size() + 1);
+    pa_allocator::Seq s;
+    s.blocks.reserve(need);
+    pa_allocator::Seq& dst = a->seqs.emplace(seq, pa_allocator::Seq{}).first->second;
+    for (int64_t i = 0; i < need; ++i) s.blocks.push_back(a->take());
+    s.ctx = num_tokens;
+    dst = std::move(s);
+    a->arrival.push_back(seq);
+    return ok();
+  })
 }
 
 extern "C" pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const int32_t* tokens,
@@ -177,6 +201,7 @@ extern "C" pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const 
   const int32_t bs = a->block_size;
   const int64_t need = (static_cast<int64_t>(num_tokens) + bs - 1) / bs;
   const int64_t full = num_tokens / bs;
+  PA_GUARDED(fn, {
   // chain keys of every full block, and the leading run of cache hits
   std::vector<uint64_t> keys(full);
   std::vector<int32_t> hits;
@@ -199,14 +224,27 @@ extern "C" pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const 
   if (need - static_cast<int64_t>(hits.size()) + claimed > a->nfree)
     return fail(PA_ERR_OUT_OF_BLOCKS, "%s: sequence %d needs %lld new blocks, %d free", fn, seq,
                 static_cast<long long>(need - static_cast<int64_t>(hits.size()) + claimed), a->nfree);
+  // every allocation before the first change: the key arrays (built aside
+  // and moved in whole), map nodes for the new keys (moved into the cache
+  // later without allocating), the table, the arrival slot, the sequence
   if (a->keyed.empty()) {
-    a->keyed.assign(a->num_blocks, 0);
-    a->key_hash.assign(a->num_blocks, 0);
-    a->key_parent.assign(a->num_blocks, 0);
-    a->key_tokens.assign(static_cast<size_t>(a->num_blocks) * bs, 0);
+    std::vector<uint8_t> keyed(a->num_blocks, 0);
+    std::vector<uint64_t> key_hash(a->num_blocks, 0), key_parent(a->num_blocks, 0);
+    std::vector<int32_t> key_tokens(static_cast<size_t>(a->num_blocks) * bs, 0);
+    a->keyed = std::move(keyed);
+    a->key_hash = std::move(key_hash);
+    a->key_parent = std::move(key_parent);
+    a->key_tokens = std::move(key_tokens);
   }
+  // (a node for every new full block: taking a block below can drop a key
+  // the cache holds now, and such a key is then inserted like any other)
+  std::unordered_map<uint64_t, int32_t> fresh;
+  for (int64_t j = static_cast<int64_t>(hits.size()); j < full; ++j) fresh.emplace(keys[j], -1);
+  a->cache.reserve(a->cache.size() + fresh.size());
+  a->arrival.reserve(a->arrival.size() + 1);
   pa_allocator::Seq s;
   s.blocks.reserve(need);
+  pa_allocator::Seq& dst = a->seqs.emplace(seq, pa_allocator::Seq{}).first->second;
   for (int32_t b : hits) {
     if (a->refcount[b] == 0) a->unlink_free(b);
     a->refcount[b] += 1;
@@ -216,7 +254,9 @@ extern "C" pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const 
     const int32_t b = a->take();
     s.blocks.push_back(b);
     if (j < full && !a->cache.count(keys[j])) {
-      a->cache.emplace(keys[j], b);
+      auto node = fresh.extract(keys[j]);  // present: one node per distinct key, used at most once
+      node.mapped() = b;
+      a->cache.insert(std::move(node));
       a->keyed[b] = 1;
       a->key_hash[b] = keys[j];
       a->key_parent[b] = j > 0 ? keys[j - 1] : 0;
@@ -224,10 +264,11 @@ extern "C" pa_status pa_seq_allocate_cached(pa_allocator* a, int32_t seq, const 
     }
   }
   s.ctx = num_tokens;
-  a->seqs.emplace(seq, std::move(s));
+  dst = std::move(s);
   a->arrival.push_back(seq);
   *num_cached_tokens = static_cast<int32_t>(hits.size()) * bs;
   return ok();
+  })
 }
 
 extern "C" int32_t pa_prefix_cache_size(const pa_allocator* a) noexcept {
@@ -239,11 +280,14 @@ extern "C" pa_status pa_seq_fork(pa_allocator* a, int32_t parent, int32_t child)
   auto it = a->seqs.find(parent);
   if (it == a->seqs.end()) return fail(PA_ERR_UNKNOWN_SEQ, "pa_seq_fork: unknown parent %d", parent);
   if (a->exists(child)) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_fork: sequence %d exists", child);
-  pa_allocator::Seq s = it->second;
-  for (int32_t b : s.blocks) a->refcount[b] += 1;
-  a->seqs.emplace(child, std::move(s));
-  a->arrival.push_back(child);
-  return ok();
+  PA_GUARDED("pa_seq_fork", {
+    a->arrival.reserve(a->arrival.size() + 1);
+    pa_allocator::Seq s = it->second;
+    a->seqs.emplace(child, std::move(s));  // may rehash: `it` is not used after this
+    for (int32_t b : a->seqs.find(child)->second.blocks) a->refcount[b] += 1;
+    a->arrival.push_back(child);
+    return ok();
+  })
 }
 
 extern "C" pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* cow_src, int32_t* cow_dst) noexcept {
@@ -255,6 +299,7 @@ extern "C" pa_status pa_seq_append_slot(pa_allocator* a, int32_t seq, int32_t* c
   pa_allocator::Seq& s = it->second;
   if (s.ctx == INT32_MAX) return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_append_slot: context overflow");
   if (s.ctx % a->block_size == 0) {
+    PA_GUARDED("pa_seq_append_slot", s.blocks.reserve(s.blocks.size() + 1);)
     // the last block is full (or there is none): lazily take a new one
     if (a->nfree == 0)
       return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_append_slot: no free block for sequence %d", seq);
@@ -302,9 +347,9 @@ extern "C" pa_status pa_seq_swap_out(pa_allocator* a, int32_t seq, int32_t* bloc
   *num_blocks = static_cast<int32_t>(blocks.size());
   if (static_cast<int64_t>(blocks.size()) > cap)
     return fail(PA_ERR_INVALID_ARGUMENT, "pa_seq_swap_out: %zu blocks, room for %d", blocks.size(), cap);
+  PA_GUARDED("pa_seq_swap_out", a->swapped.emplace(seq, it->second.ctx);)
   for (size_t j = 0; j < blocks.size(); ++j) block_ids[j] = blocks[j];
   for (int32_t b : blocks) a->release(b);
-  a->swapped.emplace(seq, it->second.ctx);
   a->seqs.erase(it);
   return ok();
 }
@@ -322,15 +367,19 @@ extern "C" pa_status pa_seq_swap_in(pa_allocator* a, int32_t seq, int32_t* block
   if (need > a->nfree)
     return fail(PA_ERR_OUT_OF_BLOCKS, "pa_seq_swap_in: sequence %d needs %lld blocks, %d free", seq,
                 static_cast<long long>(need), a->nfree);
-  pa_allocator::Seq s;
-  s.ctx = sw->second;
-  for (int64_t i = 0; i < need; ++i) {
-    s.blocks.push_back(a->take());
-    block_ids[i] = s.blocks.back();
-  }
-  a->seqs.emplace(seq, std::move(s));
-  a->swapped.erase(sw);
-  return ok();
+  PA_GUARDED("pa_seq_swap_in", {
+    pa_allocator::Seq s;
+    s.blocks.reserve(need);
+    s.ctx = sw->second;
+    pa_allocator::Seq& dst = a->seqs.emplace(seq, pa_allocator::Seq{}).first->second;
+    for (int64_t i = 0; i < need; ++i) {
+      s.blocks.push_back(a->take());
+      block_ids[i] = s.blocks.back();
+    }
+    dst = std::move(s);
+    a->swapped.erase(sw);
+    return ok();
+  })
 }
 
 extern "C" pa_status pa_seq_get(const pa_allocator* a, int32_t seq, int32_t* block_ids, int32_t cap,
@@ -382,7 +431,8 @@ extern "C" pa_status pa_allocator_get_stats(const pa_allocator* a, pa_allocator_
   out->num_seqs = static_cast<int32_t>(a->seqs.size());
   // a slot holds a token when some sequence's context covers it; count each
   // physical (block, slot) once, so shared prefixes are not double counted
-  std::vector<int32_t> filled(a->num_blocks, 0);
+  std::vector<int32_t> filled;
+  PA_GUARDED("pa_allocator_get_stats", filled.assign(a->num_blocks, 0);)
   for (const auto& kv : a->seqs) {
     const auto& s = kv.second;
     for (size_t j = 0; j < s.blocks.size(); ++j) {

@@ -179,7 +179,10 @@ int resident_slots(const void* kernel, int threads) {
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess) return 0;
   const int n = cus * (per > 0 ? per : 1);
-  cache[{kernel, dev}] = n;
+  try {
+    cache[{kernel, dev}] = n;  // the answer stands even when it cannot be kept
+  } catch (...) {
+  }
   return n;
 }
 
@@ -337,7 +340,11 @@ extern "C" pa_status pa_decode_shared_prefix(const pa_kv_cache* cache, const voi
 extern "C" pa_status pa_timing_enable(int32_t on) noexcept {
   timing_release();
   if (!on) return ok();
-  g_timing.part_ev.resize(2 * kTimingSlots);
+  try {
+    g_timing.part_ev.resize(2 * kTimingSlots);
+  } catch (...) {
+    return fail(PA_ERR_HOST_MEMORY, "pa_timing_enable: out of host memory");
+  }
   for (hipEvent_t& e : g_timing.part_ev) {
     // Timing only: no system-scope fence (cache writeback and invalidation)
     // when an event completes, which would otherwise add several

@@ -29,11 +29,8 @@ struct AllocatorGuard {
   ~AllocatorGuard() { pa_allocator_destroy(a); }
 };
 
-}  // namespace
-
-extern "C" pa_status pa_simulate_arrivals(int32_t num_blocks, int32_t block_size, const int32_t* arrivals,
-                                          const int32_t* lengths, int32_t n, pa_arrival_readout* out,
-                                          int32_t* trace, int32_t trace_cap) noexcept {
+pa_status simulate(int32_t num_blocks, int32_t block_size, const int32_t* arrivals, const int32_t* lengths,
+                   int32_t n, pa_arrival_readout* out, int32_t* trace, int32_t trace_cap) {
   static const char* fn = "pa_simulate_arrivals";
   if (!out || n < 0 || num_blocks < 0 || block_size < 1 || trace_cap < 0 || (trace_cap > 0 && !trace) ||
       (n > 0 && (!arrivals || !lengths)))
@@ -139,4 +136,18 @@ extern "C" pa_status pa_simulate_arrivals(int32_t num_blocks, int32_t block_size
   out->preemptions = preemptions;
   out->utilisation = util_n ? util_sum / util_n : 0.0;
   return ok();
+}
+
+}  // namespace
+
+extern "C" pa_status pa_simulate_arrivals(int32_t num_blocks, int32_t block_size, const int32_t* arrivals,
+                                          const int32_t* lengths, int32_t n, pa_arrival_readout* out,
+                                          int32_t* trace, int32_t trace_cap) noexcept {
+  // the simulation's state is its own (vectors and an allocator it
+  // destroys), so a failed host allocation only ends it
+  try {
+    return simulate(num_blocks, block_size, arrivals, lengths, n, out, trace, trace_cap);
+  } catch (...) {
+    return fail(PA_ERR_HOST_MEMORY, "pa_simulate_arrivals: out of host memory");
+  }
 }

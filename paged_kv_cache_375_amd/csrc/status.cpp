@@ -33,6 +33,7 @@ extern "C" const char* pa_status_str(pa_status s) noexcept {
     case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_HOST_MEMORY: return "PA_ERR_HOST_MEMORY";
   }
   return "PA_ERR_UNKNOWN_STATUS";
 }
