@@ -604,8 +604,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   if (direct || PREFIX) return;
 
   // Split context: the last partition to finish merges every partial of the
-  // workgroup's heads exactly and restores the arrival counter to zero (see
-  // the per-head kernel for the memory-ordering argument).
+  // workgroup's heads exactly and restores the arrival counter to zero.
+  //
+  // Why the last arrival sees every partial, although its workgroups may run
+  // on different XCDs, each with its own L2 that is not coherent with the
+  // others.  The argument rests on the gfx942/gfx950 memory model as the
+  // LLVM AMDGPU backend documents it (AMDGPUUsage, "Memory Model GFX942"):
+  // an access with the SC1 cache-policy bit is what that backend emits for a
+  // relaxed (monotonic) atomic load or store at agent scope; it is served at
+  // the agent's point of coherence, not from a cache line of this XCD.
+  //  1. Every partial is written with SC1 stores (CoherentWindow::store*),
+  //     so each store completes at the point of coherence.
+  //  2. s_waitcnt(0) then holds each wave until all of its stores are
+  //     acknowledged (on gfx9 stores count in vmcnt and are acknowledged
+  //     once performed at the level their policy names), and the barrier
+  //     holds the workgroup until every wave has passed that wait.  Only then
+  //     does thread 0 add to the counter.
+  //  3. The counter add is an agent-scope atomic, performed at the point of
+  //     coherence, so all adds to one counter are ordered there.  The add
+  //     that returns nparts - 1 comes after every other partition's add, and
+  //     each of those was issued only after that partition's stores were
+  //     acknowledged (2).  Hence every partial is at the point of coherence
+  //     before the last add returns.
+  //  4. The last workgroup reads the partials only after its add has
+  //     returned (the barrier below and the branch on is_last; a barrier is
+  //     also a compiler fence, so no load is hoisted above it), and it reads
+  //     them with SC1 loads (CoherentWindow::load*), which are served at the
+  //     point of coherence and cannot hit a stale line of its own L1 or L2.
+  // The C++ model would ask for release/acquire on the counter; the backend
+  // lowers those to a write-back of this XCD's whole L2 (buffer_wbl2) before
+  // the add and an invalidation of it (buffer_inv) after, which steps 1 and
+  // 4 make unnecessary: only the partials cross XCDs, and they never stay in
+  // a non-coherent cache.  The counter is reset with an agent-scope store
+  // after the merge; the next launch sees it through the kernel boundary.
   const int64_t cidx = static_cast<int64_t>(s) * P.hq + h0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
