@@ -244,6 +244,30 @@ pa_status pa_decode_step(const pa_kv_cache* cache, const void* q, const void* k_
                          void* stream) PA_NOEXCEPT;
 
 /*
+ * pa_decode_step_noalloc — pa_decode_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  Same arguments, result and pool contents as
+ * pa_decode_step, without the workspace: the split-context partials and
+ * arrival counters live in a scratch array inside the library, 32 MiB on
+ * each GPU it runs on (a file-scope device array, held until the process
+ * ends).  The call allocates nothing and calls no allocating routine.
+ *
+ * A call whose pa_decode_workspace_size(num_seqs, num_q_heads, head_dim,
+ * max_context_len) exceeds 32 MiB returns PA_ERR_WORKSPACE_TOO_SMALL before
+ * anything else (pa_decode_step takes a workspace of any size).  The first
+ * call on a device that needs the scratch clears it with a kernel on
+ * `stream`, ordered before that call's decode (if `stream` is being captured,
+ * the clear is captured too and the next call outside capture clears again);
+ * every completed call leaves the counters at zero.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU race and
+ * give undefined results, whatever their streams; the caller orders them.
+ */
+pa_status pa_decode_step_noalloc(const pa_kv_cache* cache, const void* q, const void* k_new, const void* v_new,
+                                 void* out, int32_t act, int32_t num_q_heads, const int32_t* block_tables,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                 int32_t max_context_len, float sm_scale, void* stream) PA_NOEXCEPT;
+
+/*
  * pa_decode_shared_prefix — decode (and, with k_new/v_new non-NULL, the
  * append of pa_decode_step) for batches whose sequences share a prompt
  * prefix in the same physical blocks (a fork, a common system prompt, a

@@ -18,7 +18,7 @@ PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 # every symbol the public header declares
 EXPORTS = (
     "pa_kv_append", "pa_kv_write_prompt", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size", "pa_decode",
-    "pa_decode_step", "pa_decode_shared_prefix", "pa_decode_shared_workspace_size", "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free", "pa_seq_allocate",
+    "pa_decode_step", "pa_decode_step_noalloc", "pa_decode_shared_prefix", "pa_decode_shared_workspace_size", "pa_allocator_create", "pa_allocator_destroy", "pa_allocator_num_free", "pa_seq_allocate",
     "pa_seq_allocate_cached", "pa_prefix_cache_size", "pa_seq_fork", "pa_seq_append_slot", "pa_seq_free",
     "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_get", "pa_export_tables", "pa_block_refcount",
     "pa_allocator_get_stats", "pa_latest_arrival", "pa_simulate_arrivals", "pa_status_str", "pa_last_error",
@@ -78,6 +78,7 @@ def lib():
         "pa_decode": (st, [P(PaKVCache), vp, vp, i32, i32, vp, vp, i32, i32, i32, f32, vp, ctypes.c_size_t, vp]),
         "pa_decode_step": (st, [P(PaKVCache), vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, f32, vp,
                                 ctypes.c_size_t, vp]),
+        "pa_decode_step_noalloc": (st, [P(PaKVCache), vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, f32, vp]),
         "pa_decode_shared_prefix": (st, [P(PaKVCache), vp, vp, vp, vp, i32, i32, vp, vp, i32, i32, i32, f32, i32, vp,
                                          vp, vp, ctypes.c_size_t, vp]),
         "pa_decode_shared_workspace_size": (ctypes.c_size_t, [i32, i32, i32, i32, i32]),

@@ -181,6 +181,28 @@ def decode_step(cache: KVCache, q, k_new, v_new, block_tables, context_lens, max
     return out
 
 
+def decode_step_noalloc(cache: KVCache, q, k_new, v_new, block_tables, context_lens, max_context_len, sm_scale,
+                        out, stream=None):
+    """pa_decode_step with the library's own per-device scratch in place of a
+    workspace (pa_decode_step_noalloc); `out` must be given (nothing is
+    allocated)."""
+    B, hq, d = q.shape
+    act = _act(q)
+    shape = (B, cache.num_kv_heads, cache.head_dim)
+    _dev(k_new, q.dtype, "k_new", shape)
+    _dev(v_new, q.dtype, "v_new", shape)
+    _dev(q, q.dtype, "q", (B, hq, cache.head_dim))
+    _dev(block_tables, torch.int32, "block_tables")
+    _dev(context_lens, torch.int32, "context_lens", (B,))
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [num_seqs][max_blocks_per_seq]")
+    _dev(out, q.dtype, "out", q.shape)
+    check(lib().pa_decode_step_noalloc(ctypes.byref(cache.struct), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), act,
+                                       hq, _ptr(block_tables), _ptr(context_lens), B, block_tables.shape[1],
+                                       int(max_context_len), float(sm_scale), _stream(stream)))
+    return out
+
+
 def shared_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, max_shared_tokens):
     return int(lib().pa_decode_shared_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
                                                      max_shared_tokens))

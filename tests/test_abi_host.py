@@ -52,6 +52,18 @@ def _decode(c, **kw):
                                 a["mb"], a["mctx"], a["scale"], a["ws"], a["wsb"], None)
 
 
+def test_noalloc_refuses_more_scratch_than_it_holds_before_any_device_call():
+    """pa_decode_step_noalloc checks its workspace need (host arithmetic)
+    before it touches the device."""
+    c = _cache()
+    need = _lib.lib().pa_decode_workspace_size(64, 64, 128, 1 << 19)
+    assert need > 32 << 20
+    st = _lib.lib().pa_decode_step_noalloc(ctypes.byref(c), 0x3000, 0x7000, 0x8000, 0x4000, _lib.PA_F16, 64, 0x5000,
+                                            0x6000, 64, 1 << 15, 1 << 19, 0.1, None)
+    assert st == _lib.PA_ERR_WORKSPACE_TOO_SMALL
+    assert b"32" in _lib.lib().pa_last_error() or b"33554432" in _lib.lib().pa_last_error()
+
+
 def test_decode_argument_checks_fail_before_any_launch():
     L = _lib.lib()
     assert _decode(_cache(block_size=3)) == _lib.PA_ERR_UNSUPPORTED

@@ -1,0 +1,80 @@
+"""pa_decode_step_noalloc against pa_decode_step (needs an MI355X).
+
+The no-allocation entry point keeps its split-context partials and arrival
+counters in the library's own per-device scratch array.  Two calls in a row
+(the second over fewer sequences and a shorter longest context, so it reuses
+a scratch the first call left behind) must give exactly what pa_decode_step
+with a caller-owned workspace gives, output and pool, on the grouped kernel
+(in-launch merge through arrival counters) and on the per-head kernel (merge
+launch); a call needing more scratch than the library holds is refused before
+any launch.
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_375_amd import _lib, api
+from paged_kv_cache_375_amd.workloads import WORKLOADS
+from tests.gpu_helpers import TOL, build_pair, out_f64, pool_bytes
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    WORKLOADS["falcon7b_mqa"].scaled(batch=6, ctx_lo=600, ctx_hi=1300),       # grouped kernel, split contexts
+    WORKLOADS["opt13b"].scaled(batch=5, ctx_lo=600, ctx_hi=1700),             # per-head kernel + merge launch
+    WORKLOADS["opt13b_fp8_prefix"].scaled(batch=4, ctx_lo=200, ctx_hi=900),  # FP8 pool, per-head kernel
+]
+
+
+def _sub(t, n):
+    return t[:n].contiguous()
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_noalloc_step_equals_workspace_step_twice(wl):
+    print(f"[noalloc] {wl}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    if gpu.step_pairs is not None:
+        api.copy_blocks(gpu.cache, gpu.step_pairs)
+    na = gpu.cache.with_pools(gpu.cache.k.clone(), gpu.cache.v.clone())
+    n2 = max(1, wl.batch // 2)
+    max2 = int(dr.ctx[:n2].max())
+    args1 = (gpu.q, gpu.k_new, gpu.v_new, gpu.tables, gpu.ctx, gpu.max_ctx, gpu.sm_scale)
+    args2 = (_sub(gpu.q, n2), _sub(gpu.k_new, n2), _sub(gpu.v_new, n2), _sub(gpu.tables, n2), _sub(gpu.ctx, n2),
+             max2, gpu.sm_scale)
+    assert api.decode_workspace_size(wl.batch, wl.num_q_heads, wl.head_dim, gpu.max_ctx) > 0
+    assert api.decode_workspace_size(n2, wl.num_q_heads, wl.head_dim, max2) > 0
+
+    # two calls in a row on the library's scratch, nothing in between
+    got1 = api.decode_step_noalloc(na, *args1, out=torch.empty_like(gpu.q))
+    got2 = api.decode_step_noalloc(na, *args2, out=torch.empty_like(args2[0]))
+    torch.cuda.synchronize()
+    # the same two calls with caller-owned workspaces
+    want1 = api.decode_step(gpu.cache, *args1).clone()
+    want2 = api.decode_step(gpu.cache, *args2).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(got1, want1)
+    assert torch.equal(got2, want2)
+    assert torch.equal(na.k, gpu.cache.k) and torch.equal(na.v, gpu.cache.v)
+    # and both meet the bound against the reference
+    ref.append()
+    assert np.array_equal(pool_bytes(na.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(na.v), ref.v.view(np.uint8))
+    want = ref.decode()
+    err1 = float(np.max(np.abs(out_f64(got1) - want)))
+    err2 = float(np.max(np.abs(out_f64(got2) - want[:n2])))
+    print(f"[noalloc] {wl.name}: bit-identical to pa_decode_step; max abs err {err1:.3e}, {err2:.3e} "
+          f"(bound {TOL[wl.kv]})", flush=True)
+    assert max(err1, err2) <= TOL[wl.kv]
+
+
+def test_noalloc_refuses_more_scratch_than_it_holds():
+    wl = WORKLOADS["opt13b"].scaled(batch=2, ctx_lo=10, ctx_hi=40)
+    dr, gpu, ref = build_pair(wl)
+    big = 1 << 19  # 1024 partitions: 2 x 40 heads x 1024 x 130 floats > 32 MiB
+    assert api.decode_workspace_size(2, wl.num_q_heads, wl.head_dim, big) > 32 << 20
+    with pytest.raises(_lib.PagedAttnError) as e:
+        api.decode_step_noalloc(gpu.cache, gpu.q, gpu.k_new, gpu.v_new, gpu.tables, gpu.ctx, big, gpu.sm_scale,
+                                out=torch.empty_like(gpu.q))
+    assert e.value.status == _lib.PA_ERR_WORKSPACE_TOO_SMALL
+    assert "32" in str(e.value) or "33554432" in str(e.value)
