@@ -237,6 +237,50 @@ def bench_swap(wl, args):
                           "bytes": total, "higher_is_better": True, "data": "synthetic"}), flush=True)
 
 
+def bench_read_ceiling(wl, dr, step, args):
+    """The read rate this GPU reaches with no arithmetic: pa_read_probe over
+    the workload's own pools and tables, in the decode's load pattern
+    ("paged": every sequence's K and V rows through its table) and start to
+    end ("linear"), rotating over the same pool copies as the decode, beside
+    the decode step timed the same way.  One JSON line per measurement."""
+    import torch
+
+    from paged_kv_cache_375_amd import api
+    from paged_kv_cache_375_amd.accounting import ELEM_BYTES
+
+    sc = step.scenario
+    ek = ELEM_BYTES[wl.kv]
+    row = wl.num_kv_heads * wl.head_dim * ek
+    paged_bytes = int(sc.ctx.sum()) * 2 * row
+    pool_bytes = 2 * step.cache.k.numel() * step.cache.k.element_size()
+    rotate = args.rotate or max(1, min(8, math.ceil(2e9 / paged_bytes)))
+    caches = [step.cache] + [step.cache.with_pools(step.cache.k.clone(), step.cache.v.clone())
+                             for _ in range(rotate - 1)]
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    K = args.steps
+    i = [0]
+
+    def rot():
+        i[0] += 1
+        return caches[i[0] % rotate]
+
+    runs = [("read probe, paged (the decode's load pattern)", paged_bytes,
+             lambda: api.read_probe(rot(), step.tables, step.ctx, step.max_ctx, "paged", sink)),
+            ("read probe, linear (both pools start to end)", pool_bytes,
+             lambda: api.read_probe(rot(), step.tables, step.ctx, step.max_ctx, "linear", sink)),
+            ("decode step (pa_decode_step: append + attention + merge)", paged_bytes,
+             lambda: step.run(rot()))]
+    for what, nbytes, fn in runs:
+        for _ in range(max(2, args.warmup)):
+            fn()
+        ms = _time_ms(fn, K)
+        gbps = nbytes / (ms / 1e3) / 1e9
+        print(json.dumps({"metric": "HBM read GB/s, 1 GPU", "what": what, "value": gbps, "unit": "GB/s",
+                          "frac_of_peak": gbps / HBM_PEAK_GBPS, "ms_per_call": ms, "bytes_read": nbytes,
+                          "calls": K, "pool_copies_rotated": rotate,
+                          "config": {"workload": workload_label(wl), "sum_ctx": int(sc.ctx.sum())}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +299,9 @@ def main():
                          "and print one JSON line per writer")
     ap.add_argument("--no-shared", action="store_true",
                     help="decode a prefix workload with pa_decode_step like any other, not the shared-prefix path")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="instead of the decode step, time pa_read_probe (the pools read with the decode's load "
+                         "pattern and start to end, no arithmetic) beside the decode step")
     ap.add_argument("--swap", action="store_true",
                     help="instead of the decode step, time block swaps to pinned host memory and back for each "
                          "block size (the workload's heads, head_dim and pool dtype)")
@@ -297,6 +344,9 @@ def main():
     step = DecodeStep(dr, "cuda")
     if args.writers:
         bench_writers(wl, dr, step, args)
+        return
+    if args.read_ceiling:
+        bench_read_ceiling(wl, dr, step, args)
         return
     sc = step.scenario
     sb = step_bytes(sc.ctx, sc.tables, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.block_size, wl.act, wl.kv,

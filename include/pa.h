@@ -452,6 +452,25 @@ const char* pa_last_error(void) PA_NOEXCEPT;
 pa_status pa_timing_enable(int32_t on) PA_NOEXCEPT;
 pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches) PA_NOEXCEPT;
 
+/*
+ * pa_read_probe — measurement only: the rate at which this GPU reads the
+ * pools, without any of the decode's arithmetic, so that the decode kernels
+ * can be judged against what their access pattern allows.  mode 0 runs the
+ * per-head decode kernel with its arithmetic compiled out, treating every KV
+ * head as one query head: the same grid, table staging and 16-byte
+ * non-temporal K and V loads, every sequence's rows read through its block
+ * table in logical order [F55 §块表] (entries outside [0, num_blocks) make
+ * that sequence read nothing).  mode 1 reads both whole pools from start to
+ * end, each workgroup one contiguous span (tables and lengths are ignored).
+ * Each lane folds its loaded words with XOR and writes sink (device, uint32
+ * [1024], caller-owned) only if the fold equals a fixed value, so the loads
+ * cannot be dropped; the sink's contents mean nothing.  Asynchronous on
+ * stream.
+ */
+pa_status pa_read_probe(const pa_kv_cache* cache, const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t mode,
+                        uint32_t* sink, void* stream) PA_NOEXCEPT;
+
 #ifdef __cplusplus
 }
 #endif

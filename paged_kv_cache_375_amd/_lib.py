@@ -22,7 +22,7 @@ EXPORTS = (
     "pa_seq_allocate_cached", "pa_prefix_cache_size", "pa_seq_fork", "pa_seq_append_slot", "pa_seq_free",
     "pa_seq_swap_out", "pa_seq_swap_in", "pa_seq_get", "pa_export_tables", "pa_block_refcount",
     "pa_allocator_get_stats", "pa_latest_arrival", "pa_simulate_arrivals", "pa_status_str", "pa_last_error",
-    "pa_timing_enable", "pa_timing_read",
+    "pa_timing_enable", "pa_timing_read", "pa_read_probe",
 )
 
 
@@ -103,6 +103,7 @@ def lib():
         "pa_last_error": (ctypes.c_char_p, []),
         "pa_timing_enable": (st, [i32]),
         "pa_timing_read": (st, [P(ctypes.c_double), P(i32)]),
+        "pa_read_probe": (st, [P(PaKVCache), vp, vp, i32, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

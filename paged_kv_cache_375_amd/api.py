@@ -238,6 +238,16 @@ def decode_shared_prefix(cache: KVCache, q, block_tables, context_lens, max_cont
     return out
 
 
+def read_probe(cache: KVCache, block_tables, context_lens, max_context_len, mode, sink, stream=None):
+    """Measurement only (pa_read_probe): read the pools with the decode's load
+    pattern (mode 0, "paged") or start to end (mode 1, "linear")."""
+    mode = {"paged": 0, "linear": 1}.get(mode, mode)
+    _dev(sink, torch.int32, "sink", (1024,))
+    B = context_lens.shape[0]
+    check(lib().pa_read_probe(ctypes.byref(cache.struct), _ptr(block_tables), _ptr(context_lens), B,
+                              block_tables.shape[1], int(max_context_len), int(mode), _ptr(sink), _stream(stream)))
+
+
 def timing_enable(on=True):
     check(lib().pa_timing_enable(1 if on else 0))
 

@@ -337,6 +337,25 @@ extern "C" pa_status pa_decode_shared_prefix(const pa_kv_cache* cache, const voi
                        workspace_bytes, stream, num_groups, group_start, group_shared_blocks);
 }
 
+extern "C" pa_status pa_read_probe(const pa_kv_cache* cache, const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t mode,
+                                   uint32_t* sink, void* stream) noexcept {
+  static const char* fn = "pa_read_probe";
+  if (pa_status s = check_cache(cache, fn)) return s;
+  if (mode != 0 && mode != 1) return fail(PA_ERR_INVALID_ARGUMENT, "%s: mode %d", fn, mode);
+  if (!sink) return fail(PA_ERR_INVALID_ARGUMENT, "%s: sink is NULL", fn);
+  if (mode == 0) {
+    if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0)
+      return fail(PA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
+    if (num_seqs > kMaxGridYZ || (max_context_len + 511) / 512 > kMaxGridYZ)
+      return fail(PA_ERR_UNSUPPORTED, "%s: grid too large", fn);
+    if (num_seqs > 0 && (!block_tables || !context_lens)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL table", fn);
+  }
+  return hip_status(pa::launch_read_probe(*cache, block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                          max_context_len, mode, sink, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 extern "C" pa_status pa_timing_enable(int32_t on) noexcept {
   timing_release();
   if (!on) return ok();

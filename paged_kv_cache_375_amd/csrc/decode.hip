@@ -35,9 +35,12 @@ namespace {
 // Launch shape: wavefronts per workgroup (measured best: eight for f16 and
 // f32 pools, two for FP8 pools, whose lanes do more arithmetic per byte) and
 // wave loads per batch.
+#ifndef PA_DECODE_WAVES_F16
+#define PA_DECODE_WAVES_F16 8
+#endif
 template <typename KV>
 constexpr int decode_waves() {
-  return Elem<KV>::bytes == 1 ? 2 : 8;
+  return Elem<KV>::bytes == 1 ? 2 : PA_DECODE_WAVES_F16;
 }
 #ifndef PA_DECODE_UNROLL
 #define PA_DECODE_UNROLL 8
@@ -209,7 +212,10 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* acc, floa
 // shared prefix (whose pass left partials in slots 0 .. pre - 1), leaves a
 // partial per partition in slot pre + p for merge_kernel; a head with a
 // single partial writes its output.
-template <typename KV, typename ACT, int D, int NW, int U, bool BIG>
+// LOADS_ONLY (measurement, pa_read_probe): the same grid, table staging and
+// K/V loads, with the arithmetic replaced by an XOR of the loaded words into
+// P.out (a uint32 sink of kProbeSinkWords words); nothing else is written.
+template <typename KV, typename ACT, int D, int NW, int U, bool BIG, bool LOADS_ONLY = false>
 __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   using M = Math<KV, ACT>;
   constexpr int EPL = M::EPL;
@@ -247,7 +253,8 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   const int64_t block_rows = static_cast<int64_t>(P.hkv) * bs;  // token rows per block
 
   // q is loaded first, so its latency overlaps the table slice's
-  const typename M::Q qr = M::load_q(static_cast<const ACT*>(P.q) + sh * D + c * EPL);
+  typename M::Q qr{};
+  if constexpr (!LOADS_ONLY) qr = M::load_q(static_cast<const ACT*>(P.q) + sh * D + c * EPL);
 
   __shared__ int tab[BIG ? 1 : PART];
   __shared__ float red_m[NW], red_l[NW];
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   // takes its K/V from the caller's rows, not from the pool, and the kv
   // head's first query head stores them into the pool slot.  Nothing in this
   // launch reads that slot from the pool.
-  const bool has_new = P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
+  const bool has_new = !LOADS_ONLY && P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
   Vec16 knew{{0, 0, 0, 0}}, vnew{{0, 0, 0, 0}};
   if (has_new) {
     const int64_t src = (static_cast<int64_t>(s) * P.hkv + g) * D * static_cast<int64_t>(sizeof(ACT));
@@ -313,6 +320,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
   const int nrounds = bad_early ? 0 : (t1 - t0 + ROUND - 1) / ROUND;
+  uint32_t fold = 0;  // LOADS_ONLY
   for (int r0 = 0; r0 < nrounds; r0 += U) {
     Vec16 kr[U], vr[U];
     int tok[U];
@@ -339,6 +347,12 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
       vr[u] = load16_stream(P.vc + off);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (LOADS_ONLY) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        fold ^= kr[u].w[0] ^ kr[u].w[1] ^ kr[u].w[2] ^ kr[u].w[3] ^ vr[u].w[0] ^ vr[u].w[1] ^ vr[u].w[2] ^ vr[u].w[3];
+      continue;
+    }
     if (has_new && r0 + U >= nrounds) {  // the batch that holds the new token
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -374,6 +388,13 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
     m = m_new;
   }
 
+  if constexpr (LOADS_ONLY) {
+    // the loads cannot be dropped: the store depends on their values (and
+    // almost never happens, so the sink adds no traffic)
+    if (fold == kProbeMagic)
+      static_cast<uint32_t*>(P.out)[(blockIdx.x + 37 * blockIdx.y + 101 * blockIdx.z + tid) & (kProbeSinkWords - 1)] = fold;
+    return;
+  }
   // merge the rows of the wave (lanes that differ in the bits above LPT)
 #pragma unroll
   for (int o = LPT; o < 64; o <<= 1) {
@@ -531,6 +552,34 @@ hipError_t decode_t(const DecodeArgs& a) {
   return e;
 }
 
+// The per-head kernel's loads alone over a pool of element size KVB bytes
+// (pa_read_probe, paged mode): every KV head decoded as if it had one query
+// head, with f16 or f32 arithmetic types standing for the row length only.
+template <typename KV, typename ACT, int D>
+hipError_t probe_t(const DecodeArgs& a, uint32_t* sink) {
+  constexpr int NW = decode_waves<KV>(), U = PA_DECODE_UNROLL;
+  constexpr int TPL = 64 / (D / Math<KV, ACT>::EPL);
+  DecodeParams P = make_decode_params(a);
+  P.out = sink;
+  P.k_new = P.v_new = nullptr;
+  const unsigned np = static_cast<unsigned>(decode_grid_parts(a, kPartitionTokens));
+  const dim3 grid(PA_GRID_HEAD_FIRST ? a.num_q_heads : np, PA_GRID_HEAD_FIRST ? np : a.num_q_heads, a.num_seqs);
+  auto kern = a.cache->block_size >= TPL ? decode_kernel<KV, ACT, D, NW, U, true, true>
+                                         : decode_kernel<KV, ACT, D, NW, U, false, true>;
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), 0, a.stream, P);
+  return hipGetLastError();
+}
+
+template <typename KV, typename ACT>
+hipError_t probe_d(const DecodeArgs& a, uint32_t* sink) {
+  switch (a.cache->head_dim) {
+    case 32: return probe_t<KV, ACT, 32>(a, sink);
+    case 64: return probe_t<KV, ACT, 64>(a, sink);
+    case 128: return probe_t<KV, ACT, 128>(a, sink);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename KV, typename ACT>
 hipError_t decode_d(const DecodeArgs& a) {
   switch (a.cache->head_dim) {
@@ -542,6 +591,15 @@ hipError_t decode_d(const DecodeArgs& a) {
 }
 
 }  // namespace
+
+hipError_t launch_decode_loads(const DecodeArgs& a, uint32_t* sink) {
+  if (a.num_seqs == 0 || a.num_q_heads == 0) return hipSuccess;
+  const int kv = a.cache->kv_dtype;
+  if (kv == PA_F32) return probe_d<float, float>(a, sink);
+  if (kv == PA_F16) return probe_d<half_t, half_t>(a, sink);
+  if (kv == PA_FP8_E4M3) return probe_d<fp8_t, half_t>(a, sink);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_decode(const DecodeArgs& a) {
   if (a.num_seqs == 0 || a.num_q_heads == 0) return hipSuccess;

@@ -27,6 +27,17 @@ hipError_t launch_copy_blocks(const pa_kv_cache& c, const int32_t* pairs, int n,
 hipError_t launch_swap_blocks(const pa_kv_cache& c, void* host_k, void* host_v, const int32_t* ids, int n,
                               bool to_host, hipStream_t st);
 
+// Measurement only (pa_read_probe): read the pools with the decode's load
+// pattern (mode 0) or start to end (mode 1), folding into a sink of
+// kProbeSinkWords words.
+constexpr int kProbeSinkWords = 1024;
+constexpr uint32_t kProbeMagic = 0x9E3779B9u;  // a lane stores its fold only when it equals this
+// The per-head decode kernel's loads alone (paged mode of pa_read_probe).
+struct DecodeArgs;
+hipError_t launch_decode_loads(const DecodeArgs& a, uint32_t* sink);
+hipError_t launch_read_probe(const pa_kv_cache& c, const int32_t* tables, const int32_t* ctx, int num_seqs,
+                             int max_blocks, int max_ctx, int mode, uint32_t* sink, hipStream_t st);
+
 // Shared prefixes (see pa_decode_shared_prefix): at most this many groups
 // per call; the prefix pass splits each prefix into partitions of
 // kPrefixPartTokens tokens.

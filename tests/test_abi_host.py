@@ -88,6 +88,22 @@ def test_decode_argument_checks_fail_before_any_launch():
     assert b"max_context_len" in L.pa_last_error()
 
 
+def test_read_probe_argument_checks_fail_before_any_launch():
+    L = _lib.lib()
+    c = _cache()
+
+    def probe(mode=0, sink=0x9000, B=2, mctx=64, tables=0x5000, ctx=0x6000):
+        return L.pa_read_probe(ctypes.byref(c), tables, ctx, B, 4, mctx, mode, sink, None)
+
+    assert probe(mode=2) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert b"mode" in L.pa_last_error()
+    assert probe(sink=None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert probe(B=-1) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert probe(tables=None) == _lib.PA_ERR_INVALID_ARGUMENT
+    assert probe(mctx=1 << 30) == _lib.PA_ERR_UNSUPPORTED
+    assert probe(B=0) == _lib.PA_OK  # nothing to read, nothing launched
+
+
 def test_append_and_copy_argument_checks():
     L = _lib.lib()
     c = _cache()
