@@ -43,6 +43,7 @@
 #include <cmath>
 
 #include "decode_common.h"
+#include "mfma_common.h"
 
 namespace pa {
 namespace {
@@ -50,69 +51,15 @@ namespace {
 #ifndef PA_GROUP_WAVES
 #define PA_GROUP_WAVES 4
 #endif
+#ifndef PA_GROUP_ROWMAX_SWAP
+#define PA_GROUP_ROWMAX_SWAP 1
+#endif
 // Minimum waves per SIMD the register allocation must allow: three where
 // the head tiles fit without spilling, else two.
 template <int D, int HT>
 constexpr int group_occupancy() {
   return D >= 128 || (D == 64 && HT >= 3) ? 2 : 3;
 }
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-
-constexpr int kChunk = 32;  // tokens per chunk: two 16-row tiles of the first product
-constexpr float kLazy = 8.f;  // running-max slack, log2 units (weights <= 256)
-
-__device__ __forceinline__ float4_t mfma16x16x32(const half8_t& a, const half8_t& b, const float4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ half8_t as_half8(const Vec16& v) { return __builtin_bit_cast(half8_t, v); }
-
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) short4_t lds_short4_t;
-
-// Transposing LDS read of 8 bytes per lane (see the header comment).
-__device__ __forceinline__ short4_t lds_read_tr16(const void* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(const_cast<void*>(p)));
-}
-
-// exp2 on the hardware unit (inputs here are <= 0 or -inf; results below the
-// smallest normal float may flush to zero, which no weight here relies on)
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Eight E4M3 numbers (two 32-bit words) -> eight f16 (exact: every E4M3
-// value is an f16 value).
-__device__ __forceinline__ half8_t e4m3x8_to_half8(uint32_t lo, uint32_t hi) {
-  half8_t r;
-  const uint32_t w[2] = {lo, hi};
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float2_t a = e4m3x2_to_f32(w[i], false), b = e4m3x2_to_f32(w[i], true);
-    r[4 * i] = static_cast<_Float16>(a[0]);
-    r[4 * i + 1] = static_cast<_Float16>(a[1]);
-    r[4 * i + 2] = static_cast<_Float16>(b[0]);
-    r[4 * i + 3] = static_cast<_Float16>(b[1]);
-  }
-  return r;
-}
-
-template <typename KV, int D>
-struct Layout {
-  static constexpr int KVB = Elem<KV>::bytes;
-  static constexpr int NS = D / 32;             // k-steps of the first product
-  static constexpr int NDT = D / 16;            // 16-wide head_dim tiles of the second
-  static constexpr int VCH = D * KVB / 16;      // 16-byte pool chunks per token row
-  static constexpr int NV = kChunk * VCH / 64;  // loads per lane per chunk, each of K and V
-  static constexpr int LCH = D / 8;             // 16-byte f16 chunks per LDS row
-  static_assert(NV >= 1 && (kChunk * VCH) % 64 == 0, "head_dim does not fit the load layout");
-  // XOR swizzles of the 16-byte chunks of LDS row r.  K rows are read as
-  // operand rows (16 consecutive rows, one chunk each): the row's low bits.
-  // V rows are read by transposing reads (eight rows, a 32-byte column pair
-  // each): twice the row's low bits.  Both keep the reads off shared banks.
-  static __device__ __forceinline__ int swz_k(int r) { return r & (LCH - 1); }
-  static __device__ __forceinline__ int swz_v(int r) { return (2 * r) & (LCH - 2); }
-};
 
 // PREFIX = false: decode, one workgroup per (KV head and group of query
 // heads, partition, sequence), as described above.
@@ -220,9 +167,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   // each wave's K, then V, chunk as f16 rows; afterwards the merge's scratch
   constexpr int kVbuf = NW * kChunk * LCH > kMergeCap / 2 ? NW * kChunk * LCH : kMergeCap / 2;
   __shared__ uint4 vbuf[kVbuf];
-  // one wave's partial result, for the merge: 16 and 8 bytes per lane
-  __shared__ float4_t mbo[HT * NDT][64];
-  __shared__ float2_t mbl[HT][64];
+  // the waves' merge by tile (see below): per round, the states of XR tiles
+  // from the NW - 1 waves that do not own them, 16 and 8 bytes per lane
+  constexpr int XR = HT < (D >= 128 ? 1 : 2) ? HT : (D >= 128 ? 1 : 2);
+  static_assert(XR <= NW, "owners of one round must differ");
+  __shared__ float4_t xo[XR * (NW - 1) * NDT][64];
+  __shared__ float2_t xml[XR * (NW - 1)][64];
   __shared__ int is_last;
   __shared__ Vec16 newkv[2][VCH];  // the new token's K and V rows in pool format
   __shared__ uint4 qs[HT * 16 * LCH];  // the workgroup's q rows (f16), zero past the group
@@ -447,9 +397,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
       float mloc = sc[ht][0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[ht][j]);
+#if PA_GROUP_ROWMAX_SWAP
+      mloc = max_over_rows(mloc) * sscale;
+#else
       mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
       mloc *= sscale;
+#endif
       const bool raise = mloc > m[ht] + kLazy;  // uniform within a head column
       if (__any(raise)) {
         const float m_new = raise ? mloc : m[ht];
@@ -513,42 +467,57 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
 
   // each head's weight sum over the wave's four lane groups
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    lsum[ht] += __shfl_xor(lsum[ht], 16);
-    lsum[ht] += __shfl_xor(lsum[ht], 32);
-  }
+  for (int ht = 0; ht < HT; ++ht) lsum[ht] = sum_over_rows(lsum[ht]);
 
-  // merge the wavefronts' partial results in a fixed order: wave NW-1 into
-  // NW-2, ..., 1 into 0 (lane l merges with lane l; layouts are identical)
-  for (int src = NW - 1; src >= 1; --src) {
-    if (w == src) {
+  // Merge the waves' partial results by head tile: tile t belongs to wave
+  // t % NW.  In each round of XR tiles every other wave writes its state of
+  // the round's tiles to LDS at once, and each owner merges the NW - 1 states
+  // of its tile in a fixed order (the waves after it, cyclically), so results
+  // are deterministic; every wave then stores the tiles it owns.  (A chain
+  // of NW - 1 pairwise merges through one wave had each step move a whole
+  // wave's state through LDS.)
+  constexpr int NROUND = (HT + XR - 1) / XR;
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        mbl[ht][lane] = float2_t{m[ht], lsum[ht]};
+  for (int r = 0; r < NROUND; ++r) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) mbo[ht * NDT + dt][lane] = o[ht][dt];
+    for (int i = 0; i < XR; ++i) {
+      const int t = r * XR + i;
+      if (t < HT && w != t % NW) {
+        const int k = (w - t % NW - 1 + NW) % NW;
+        xml[i * (NW - 1) + k][lane] = float2_t{m[t], lsum[t]};
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) xo[(i * (NW - 1) + k) * NDT + dt][lane] = o[t][dt];
       }
     }
     __syncthreads();
-    if (w == src - 1) {
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        const float2_t ml = mbl[ht][lane];
-        const float mo = ml[0], lo = ml[1];
-        const float mn = fmaxf(m[ht], mo);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;
-        const float a = exp2f(m[ht] - mu), b = exp2f(mo - mu);
-        lsum[ht] = lsum[ht] * a + lo * b;
-        m[ht] = mn;
+    for (int i = 0; i < XR; ++i) {
+      const int t = r * XR + i;
+      if (t < HT && w == t % NW) {
+        float2_t ml[NW - 1];
+        float M = m[t];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const float4_t y = mbo[ht * NDT + dt][lane];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[ht][dt][i] = o[ht][dt][i] * a + y[i] * b;
+        for (int k = 0; k < NW - 1; ++k) {
+          ml[k] = xml[i * (NW - 1) + k][lane];
+          M = fmaxf(M, ml[k][0]);
         }
+        const float mu = (M == -INFINITY) ? 0.f : M;
+        const float a = exp2f(m[t] - mu);
+        float L = lsum[t] * a;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[t][dt] *= a;
+#pragma unroll
+        for (int k = 0; k < NW - 1; ++k) {
+          const float bk = exp2f(ml[k][0] - mu);
+          L += ml[k][1] * bk;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) o[t][dt] += bk * xo[(i * (NW - 1) + k) * NDT + dt][lane];
+        }
+        lsum[t] = L;
+        m[t] = M;
       }
     }
-    __syncthreads();
+    if (r + 1 < NROUND) __syncthreads();  // the next round rewrites the exchange
   }
 
   half_t* out = static_cast<half_t*>(P.out);
@@ -562,11 +531,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   const uint32_t rows_span = static_cast<uint32_t>((nh - 1) * static_cast<int64_t>(P.max_parts) + 1);
   const CoherentWindow wso(P.ws_o + (row0 * P.max_parts + slot) * D, rows_span * (D * 4u));
   const CoherentWindow wsml(P.ws_ml + (row0 * P.max_parts + slot) * 2, rows_span * 8u);
-  if (w == 0) {
+  {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const int hh = 16 * ht + n;
-      if (hh >= nh) continue;
+      if (ht % NW != w || hh >= nh) continue;  // the owner stores its tile
       const int64_t sh = row_sh(hh);
       const float mx = bad ? NAN : m[ht];
       const float lx = bad ? NAN : lsum[ht];
