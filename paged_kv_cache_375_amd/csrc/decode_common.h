@@ -173,24 +173,6 @@ struct NewChunk<fp8_t, float> {  // 16 numbers = 64 bytes of f32
   }
 };
 
-// Store the new token's K and V (pool format) into its slot: the first
-// D * sizeof(KV) / 16 threads each move one 16-byte chunk.  Sequences whose
-// table entry is out of range store nothing.
-template <typename KV, typename ACT, int D>
-__device__ __forceinline__ void store_new_token(const DecodeParams& P, int s, int g, int ctx, int tid) {
-  constexpr int CHUNKS = D * Elem<KV>::bytes / 16;
-  if (tid >= CHUNKS) return;
-  const int pos = ctx - 1;
-  const int bs = 1 << P.log2_bs;
-  const int b = P.tables[static_cast<int64_t>(s) * P.max_blocks + (pos >> P.log2_bs)];
-  if (b < 0 || b >= P.num_blocks) return;
-  const int64_t src = (static_cast<int64_t>(s) * P.hkv + g) * D * static_cast<int64_t>(sizeof(ACT));
-  const int64_t tok_row = (static_cast<int64_t>(b) * P.hkv + g) * bs + (pos & (bs - 1));
-  const size_t off = static_cast<size_t>(tok_row * D) * Elem<KV>::bytes + tid * 16;
-  store16(P.kw + off, NewChunk<KV, ACT>::load(P.k_new + src, tid, P.k_inv));
-  store16(P.vw + off, NewChunk<KV, ACT>::load(P.v_new + src, tid, P.v_inv));
-}
-
 }  // namespace pa
 
 namespace pa {
@@ -239,7 +221,9 @@ constexpr int kMergeCap = kMaxPartitions;
 // possibly on another XCD), 8 or 16 bytes at a time; each thread issues
 // the loads of up to U output items before it uses any, so one memory
 // latency serves them all.  The sum over partitions runs in partition
-// order whatever U is.  mw, ww: LDS scratch of kMergeCap floats each.  NT
+// order whatever U is.  With at most four partitions the first U items'
+// partials are loaded together with the (m, l) pairs, so the merge costs one
+// memory latency.  mw, ww: LDS scratch of kMergeCap floats each.  NT
 // threads take part; the caller synchronises before the call.
 template <typename ACT, int D, int NT, int U = 1>
 __device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh0, int nh, int slot0, int nparts,
@@ -256,6 +240,24 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh
   for (int hbase = 0; hbase < nh; hbase += hb) {
     const int nb = min(hb, nh - hbase);
     const int pairs = nb * nparts;
+    // four consecutive output elements per item
+    const int items = nb * (D / 4);
+    auto item_off = [&](int i, int q) -> uint32_t {
+      const int hh = i / (D / 4), d = (i - hh * (D / 4)) * 4;
+      return static_cast<uint32_t>(((hbase + hh) * stride + q) * D + d) * 4u;
+    };
+    auto load_items = [&](float4_t (&x)[U][4], int i0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = min(i0 + u * NT, items - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (q < nparts) x[u][q] = wo.load4(item_off(i, q));
+      }
+    };
+    const bool few = nparts <= 4;
+    float4_t x0[U][4];
+    if (few) load_items(x0, tid);
     for (int i0 = tid; i0 < pairs; i0 += 2 * NT) {
       float2_t x[2];
 #pragma unroll
@@ -287,28 +289,14 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh
       for (int q = 0; q < nparts; ++q) ww[hh * nparts + q] = mw[hh * nparts + q] * inv;
     }
     __syncthreads();
-    // four consecutive output elements per item
-    const int items = nb * (D / 4);
-    auto item_off = [&](int i, int q) -> uint32_t {
-      const int hh = i / (D / 4), d = (i - hh * (D / 4)) * 4;
-      return static_cast<uint32_t>(((hbase + hh) * stride + q) * D + d) * 4u;
-    };
     auto finish = [&](int i, const float4_t& acc) {
       const int hh = i / (D / 4), d = (i - hh * (D / 4)) * 4;
       const int64_t sh = sh0 + hbase + hh;
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[sh * D + d + e] = from_f32<ACT>(acc[e]);
     };
-    if (nparts <= 4) {
-      for (int i0 = tid; i0 < items; i0 += U * NT) {
-        float4_t x[U][4];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int i = min(i0 + u * NT, items - 1);
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (q < nparts) x[u][q] = wo.load4(item_off(i, q));
-        }
+    if (few) {
+      auto combine = [&](const float4_t (&x)[U][4], int i0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int i = i0 + u * NT;
@@ -320,6 +308,12 @@ __device__ __forceinline__ void merge_partials(const DecodeParams& P, int64_t sh
             if (q < nparts) acc += w[q] * x[u][q];
           finish(i, acc);
         }
+      };
+      combine(x0, tid);
+      for (int i0 = tid + U * NT; i0 < items; i0 += U * NT) {
+        float4_t x[U][4];
+        load_items(x, i0);
+        combine(x, i0);
       }
     } else {
       for (int i = tid; i < items; i += NT) {

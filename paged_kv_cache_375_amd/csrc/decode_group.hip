@@ -177,51 +177,54 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   __shared__ Vec16 newkv[2][VCH];  // the new token's K and V rows in pool format
   __shared__ uint4 qs[HT * 16 * LCH];  // the workgroup's q rows (f16), zero past the group
 
-  int my_bad = bad_len ? 1 : 0;
-  {
-    const int nb = t1 > t0 ? ((t1 - 1) >> log2_bs) - b0 + 1 : 0;
-    for (int i = tid; i < nb; i += NW * 64) {
-      int b = P.tables[trow + b0 + i];
-      if (b < 0 || b >= P.num_blocks) {
-        my_bad = 1;
-        b = 0;
-      }
-      tab[i] = b;
-    }
-  }
-  // Fused append: the workgroup of the KV head's first query group stores the
-  // new token into its slot; every workgroup reading the new token takes it
-  // from the caller's rows instead of the pool.
+  // Fused append: every workgroup reading the new token takes it from the
+  // caller's rows (staged in LDS in pool format) instead of the pool, and the
+  // workgroup of the KV head's first query group stores it into its slot
+  // after its main loop.
   const bool has_new = !PREFIX && P.k_new != nullptr && p == nparts - 1 && !bad_len && ctx >= 1;
-  if (has_new && grp == 0 && w == 0) store_new_token<KV, half_t, D>(P, s, kvh, ctx, lane);
   // Scores stay unscaled until the exponent.  A negative scale is folded
   // into q (negation is exact), so the scale applied there, |score_scale|,
   // keeps the order of the scores.
   const bool qneg = P.score_scale < 0.f;
   const float sscale = fabsf(P.score_scale);
-  {
-    // every q load of a thread is issued before the first LDS store
-    constexpr int QN = (HT * 16 * LCH + NW * 64 - 1) / (NW * 64);
-    uint4 x[QN];
+  // The table slice, q and the new token's rows are all loaded before the
+  // first of them is written to LDS, so the set-up costs one memory latency.
+  // Table entries are kept as read (an entry out of range makes the
+  // workgroup's result NaN and no K or V row is then loaded).
+  int my_bad = bad_len ? 1 : 0;
+  const int nb = t1 > t0 ? ((t1 - 1) >> log2_bs) - b0 + 1 : 0;
+  const int tab0 = tid < nb ? P.tables[trow + b0 + tid] : 0;
+  constexpr int QN = (HT * 16 * LCH + NW * 64 - 1) / (NW * 64);
+  uint4 x[QN];
 #pragma unroll
-    for (int k = 0; k < QN; ++k) {
-      const int i = tid + k * NW * 64, hh = i / LCH, ch = i % LCH;
-      x[k] = make_uint4(0, 0, 0, 0);
-      if (i < HT * 16 * LCH && hh < nh)
-        x[k] = *reinterpret_cast<const uint4*>(static_cast<const half_t*>(P.q) + row_sh(hh) * D + ch * 8);
-    }
-#pragma unroll
-    for (int k = 0; k < QN; ++k) {
-      const int i = tid + k * NW * 64, hh = i / LCH, ch = i % LCH;
-      if (qneg) x[k] = make_uint4(x[k].x ^ 0x80008000u, x[k].y ^ 0x80008000u, x[k].z ^ 0x80008000u, x[k].w ^ 0x80008000u);
-      if (i < HT * 16 * LCH) qs[hh * LCH + (ch ^ L::swz_k(hh))] = x[k];
-    }
+  for (int k = 0; k < QN; ++k) {
+    const int i = tid + k * NW * 64, hh = i / LCH, ch = i % LCH;
+    x[k] = make_uint4(0, 0, 0, 0);
+    if (i < HT * 16 * LCH && hh < nh)
+      x[k] = *reinterpret_cast<const uint4*>(static_cast<const half_t*>(P.q) + row_sh(hh) * D + ch * 8);
   }
+  Vec16 nkv{{0, 0, 0, 0}};
   if (has_new && tid < 2 * VCH) {
     const int64_t src = (static_cast<int64_t>(s) * P.hkv + kvh) * D * static_cast<int64_t>(sizeof(half_t));
     const int which = tid / VCH, ch = tid % VCH;
-    newkv[which][ch] = NewChunk<KV, half_t>::load((which ? P.v_new : P.k_new) + src, ch, which ? P.v_inv : P.k_inv);
+    nkv = NewChunk<KV, half_t>::load((which ? P.v_new : P.k_new) + src, ch, which ? P.v_inv : P.k_inv);
   }
+  if (tid < nb) {
+    my_bad |= tab0 < 0 || tab0 >= P.num_blocks;
+    tab[tid] = tab0;
+  }
+  for (int i = tid + NW * 64; i < nb; i += NW * 64) {  // slices longer than one entry per thread
+    const int b = P.tables[trow + b0 + i];
+    my_bad |= b < 0 || b >= P.num_blocks;
+    tab[i] = b;
+  }
+#pragma unroll
+  for (int k = 0; k < QN; ++k) {
+    const int i = tid + k * NW * 64, hh = i / LCH, ch = i % LCH;
+    if (qneg) x[k] = make_uint4(x[k].x ^ 0x80008000u, x[k].y ^ 0x80008000u, x[k].z ^ 0x80008000u, x[k].w ^ 0x80008000u);
+    if (i < HT * 16 * LCH) qs[hh * LCH + (ch ^ L::swz_k(hh))] = x[k];
+  }
+  if (has_new && tid < 2 * VCH) newkv[tid / VCH][tid % VCH] = nkv;
   const bool bad = __syncthreads_or(my_bad) != 0;
 
   // B operand of the first product: q of head 16 * ht + n at head_dim
@@ -463,6 +466,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
       load_rows(vr, P.vc, w);
     }
     for (int c = w; c < nchunks; c += NW) process_chunk(kr, vr, c, c + NW);
+  }
+  // the new token into its pool slot: the rows staged in LDS by the same
+  // threads, the block from the table slice (skipped if out of range)
+  if (has_new && grp == 0 && tid < 2 * VCH) {
+    const int pos = ctx - 1;
+    const int b = tab[(pos >> log2_bs) - b0];
+    if (b >= 0 && b < P.num_blocks) {
+      const int64_t tok_row = (static_cast<int64_t>(b) * P.hkv + kvh) * bs + (pos & (bs - 1));
+      store16((tid < VCH ? P.kw : P.vw) + static_cast<size_t>(tok_row * D) * KVB + (tid % VCH) * 16,
+              newkv[tid / VCH][tid % VCH]);
+    }
   }
 
   // each head's weight sum over the wave's four lane groups
