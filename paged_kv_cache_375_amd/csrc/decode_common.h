@@ -2,6 +2,7 @@
 // MFMA kernel): launch parameters, the new token's pool-format chunks for the
 // fused append, and device-coherent accesses to the split-context partials.
 #pragma once
+#include <cstddef>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -44,6 +45,24 @@ struct DecodeParams {
   int gparts[kMaxPrefixGroups];
   int gwg[kMaxPrefixGroups + 1];
 };
+
+// A kernel that reads its DecodeParams fields where it uses them, each read
+// behind a branch waiting for its own scalar load, pays a chain of misses
+// on a cold scalar cache, one per 64-byte line of the argument block.
+// Reading one word of each line it needs at entry, all at once, takes that
+// cost once; later field reads hit the cache.  Lines [0, lines) are read,
+// and `extra`, a kernel argument past the block (its line is read too).
+__device__ __forceinline__ void warm_args(const DecodeParams& P, int lines, int extra) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&P);
+  uint32_t x = static_cast<uint32_t>(extra);
+#pragma unroll
+  for (int i = 0; i < static_cast<int>(sizeof(DecodeParams) / 4); i += 16)
+    if (i < lines * 16) x ^= w[i];
+  asm volatile("" ::"s"(x));
+}
+// Lines holding every field before the shared-prefix arrays.
+constexpr int kArgHeadLines = (offsetof(DecodeParams, gstart) + 63) / 64;
+constexpr int kArgAllLines = (static_cast<int>(sizeof(DecodeParams)) + 63) / 64;
 
 // Where sequence s's own tokens begin, and how many prefix partials precede
 // its partitions' slots (both 0 outside every shared-prefix group).

@@ -51,15 +51,35 @@ namespace {
 #ifndef PA_GROUP_WAVES
 #define PA_GROUP_WAVES 4
 #endif
-#ifndef PA_GROUP_ROWMAX_SWAP
-#define PA_GROUP_ROWMAX_SWAP 1
-#endif
 // Minimum waves per SIMD the register allocation must allow: three where
 // the head tiles fit without spilling, else two.
 template <int D, int HT>
 constexpr int group_occupancy() {
   return D >= 128 || (D == 64 && HT >= 3) ? 2 : 3;
 }
+
+constexpr int kLdsPerCu = 160 * 1024;  // gfx950
+
+// LDS arena of the grouped kernel (16-byte words): the main loop's K/V
+// chunks and q rows, later the waves' merge exchange, sized to the LDS that
+// each of the workgroups one CU holds at the kernel's occupancy may use.
+template <int D, int HT, int NW>
+struct GroupArena {
+  static constexpr int LCH = D / 8, NDT = D / 16;
+  static constexpr int kVbuf = NW * kChunk * LCH > kMergeCap / 2 ? NW * kChunk * LCH : kMergeCap / 2;
+  static constexpr int kLoop = kVbuf + HT * 16 * LCH;
+  static constexpr int exchange(int xr) { return xr * (NW - 1) * NDT * 64 + (xr * (NW - 1) * 64 + 1) / 2; }
+  static constexpr int words(int xr) { return kLoop > exchange(xr) ? kLoop : exchange(xr); }
+  // LDS per workgroup when the CU holds as many as the register occupancy
+  // allows, less what the kernel keeps beside the arena (table slice, new
+  // token rows, the fold order's lengths, flags)
+  static constexpr int kBudget = kLdsPerCu / (group_occupancy<D, HT>() * 4 / NW) - kTabEntries * 4 - 2 * D * 2 -
+                                  kFoldMaxSeqs * 4 - 1024;
+  static constexpr int pick(int xr) { return xr <= 1 || words(xr) * 16 <= kBudget ? xr : pick(xr - 1); }
+  static constexpr int XR = pick(HT);
+  static constexpr int kXo = XR * (NW - 1) * NDT * 64;
+  static constexpr int kWords = words(XR);
+};
 
 // PREFIX = false: decode, one workgroup per (KV head and group of query
 // heads, partition, sequence), as described above.
@@ -75,6 +95,7 @@ constexpr int group_occupancy() {
 // launch takes them with the decode's own partials.
 template <typename KV, int D, int HT, int NW, bool UNI, bool PREFIX>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_occupancy<D, HT>()))) void decode_group_kernel(const DecodeParams P, int groups_per_kv) {
+  warm_args(P, PREFIX ? kArgAllLines : kArgHeadLines, groups_per_kv);
   using L = Layout<KV, D>;
   constexpr int KVB = L::KVB, NS = L::NS, NDT = L::NDT, NV = L::NV, LCH = L::LCH;
   constexpr int VCH = L::VCH;
@@ -88,6 +109,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   bool bad_len;
   SeqPrefix pf{0, 0};
   int gs = 0, r0 = 0;  // prefix pass: the group's first sequence, the workgroup's first row
+  int tab0 = 0;        // table entry b0 + tid of the partition's slice, if it has one
   if constexpr (PREFIX) {
     const int bx = blockIdx.x;
     int gi = 0;
@@ -135,11 +157,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
       s = __builtin_amdgcn_readfirstlane(pick);
       ctx_ranked = __builtin_amdgcn_readfirstlane(lens[s]);  // no second global read
     }
-    ctx = P.fold_order ? ctx_ranked : P.ctx[s];
     // tokens [0, begin) of a shared prefix were covered by the prefix pass
     pf = seq_prefix(P, s);
-    bad_len = seq_bad_len(P, ctx, pf);
     const int part = P.part_tokens;  // a multiple of kPartitionTokens, chosen per launch
+    // The table slice is read together with the context length, as if the
+    // context ran to the partition's end (entries past the table row are not
+    // read); entries past the real end are not used.
+    {
+      const int b0s = (pf.begin + p * part) >> log2_bs;
+      if (static_cast<int>(threadIdx.x) < (part >> log2_bs) && b0s + static_cast<int>(threadIdx.x) < P.max_blocks)
+        tab0 = P.tables[static_cast<int64_t>(s) * P.max_blocks + b0s + threadIdx.x];
+    }
+    ctx = P.fold_order ? ctx_ranked : P.ctx[s];
+    bad_len = seq_bad_len(P, ctx, pf);
     // this launch's partitions; partition 0 starts from a shared prefix's
     // merged state, so these are all the partials to merge
     nparts = bad_len ? 1 : max(1, (ctx - pf.begin + part - 1) / part);
@@ -164,18 +194,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   const int64_t block_rows = static_cast<int64_t>(P.hkv) * bs;
 
   __shared__ int tab[kTabEntries];  // the partition's table slice (part / block_size entries)
-  // each wave's K, then V, chunk as f16 rows; afterwards the merge's scratch
-  constexpr int kVbuf = NW * kChunk * LCH > kMergeCap / 2 ? NW * kChunk * LCH : kMergeCap / 2;
-  __shared__ uint4 vbuf[kVbuf];
-  // the waves' merge by tile (see below): per round, the states of XR tiles
-  // from the NW - 1 waves that do not own them, 16 and 8 bytes per lane
-  constexpr int XR = HT < (D >= 128 ? 1 : 2) ? HT : (D >= 128 ? 1 : 2);
-  static_assert(XR <= NW, "owners of one round must differ");
-  __shared__ float4_t xo[XR * (NW - 1) * NDT][64];
-  __shared__ float2_t xml[XR * (NW - 1)][64];
   __shared__ int is_last;
   __shared__ Vec16 newkv[2][VCH];  // the new token's K and V rows in pool format
-  __shared__ uint4 qs[HT * 16 * LCH];  // the workgroup's q rows (f16), zero past the group
+  // One arena serves the phases in turn.  Set-up and main loop: each wave's
+  // K, then V, chunk as f16 rows (vbuf), then the workgroup's q rows (qs, f16,
+  // zero past the group).  The waves' merge (see below): per round, the
+  // states of XR head tiles from the NW - 1 waves that do not own them (xo,
+  // xml: 16 and 8 bytes per lane).  The split-context merge: its scratch
+  // (at the start).  XR is as large as the LDS budget of the workgroups one
+  // CU holds allows, up to every tile in one round.
+  using A = GroupArena<D, HT, NW>;
+  constexpr int kVbuf = A::kVbuf, XR = A::XR;
+  static_assert(XR >= 1 && XR <= HT, "tiles per merge round");
+  __shared__ uint4 arena[A::kWords];
+  uint4* const vbuf = arena;
+  uint4* const qs = arena + kVbuf;
+  float4_t(*const xo)[64] = reinterpret_cast<float4_t(*)[64]>(arena);
+  float2_t(*const xml)[64] = reinterpret_cast<float2_t(*)[64]>(arena + A::kXo);
 
   // Fused append: every workgroup reading the new token takes it from the
   // caller's rows (staged in LDS in pool format) instead of the pool, and the
@@ -193,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   // workgroup's result NaN and no K or V row is then loaded).
   int my_bad = bad_len ? 1 : 0;
   const int nb = t1 > t0 ? ((t1 - 1) >> log2_bs) - b0 + 1 : 0;
-  const int tab0 = tid < nb ? P.tables[trow + b0 + tid] : 0;
+  if constexpr (PREFIX) tab0 = tid < nb ? P.tables[trow + b0 + tid] : 0;
   constexpr int QN = (HT * 16 * LCH + NW * 64 - 1) / (NW * 64);
   uint4 x[QN];
 #pragma unroll
@@ -228,12 +263,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   const bool bad = __syncthreads_or(my_bad) != 0;
 
   // B operand of the first product: q of head 16 * ht + n at head_dim
-  // 32 st + 8 g .. + 7, read per chunk from the workgroup's copy of q in LDS
-  // (rows swizzled like K's; zero past the group)
-  auto q_operand = [&](int ht, int st) -> half8_t {
+  // 32 st + 8 g .. + 7, from the workgroup's copy of q in LDS (rows swizzled
+  // like K's; zero past the group), held in registers for the main loop
+  half8_t qreg[HT][NS];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
     const int hh = 16 * ht + n;
-    return __builtin_bit_cast(half8_t, qs[hh * LCH + ((4 * st + g) ^ L::swz_k(hh))]);
-  };
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+      qreg[ht][st] = __builtin_bit_cast(half8_t, qs[hh * LCH + ((4 * st + g) ^ L::swz_k(hh))]);
+  }
+  auto q_operand = [&](int ht, int st) -> half8_t { return qreg[ht][st]; };
 
   float4_t o[HT][NDT];
   float m[HT], lsum[HT];
@@ -312,10 +352,51 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
       return lane_row(pool, t) + ch * 16;
     }
   };
+  // A chunk that ends inside the partition (every chunk but its last) needs
+  // no clamp.  With blocks of 16 or more tokens and at most 16 rows per wave
+  // load, a load's rows then lie in one 16-token tile: its address is the
+  // tile's wave-uniform base (the table entry times the pool's stride per
+  // block, a 32-bit product the host checks, plus the tile's first row in
+  // its block) and a per-lane offset that is the same for every chunk, so
+  // the K and V loads of a chunk share two table reads.
+  constexpr int RPL = 64 / VCH;  // token rows per wave load
+  constexpr bool FAST = UNI && RPL <= 16;
+  const uint32_t block_stride = static_cast<uint32_t>(P.hkv) * static_cast<uint32_t>(tile_bytes);
+  const uint32_t lane_const = static_cast<uint32_t>((lane / VCH) * (D * KVB) + (lane % VCH) * 16);
+  const char* const kbase = P.kc + kvh * tile_bytes;
+  const char* const vbase = P.vc + kvh * tile_bytes;
+  auto chunk_tiles = [&](int c, uint64_t (&toff)[2]) {
+    const int cb = t0 + c * kChunk;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int tt = cb + 16 * tau;
+      const uint32_t blk = __builtin_amdgcn_readfirstlane(tab[(tt >> log2_bs) - b0]);
+      toff[tau] = static_cast<uint64_t>(blk) * block_stride + static_cast<uint32_t>((tt & (bs - 1)) * (D * KVB));
+    }
+  };
+  auto load_tiles = [&](Vec16 (&x)[NV], const char* base, const uint64_t (&toff)[2]) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const char* tb = base + toff[(v * RPL) >> 4];
+      x[v] = load16_stream(tb + lane_const + ((v * RPL) & 15) * (D * KVB));
+    }
+  };
   auto load_rows = [&](Vec16 (&x)[NV], const char* pool, int c) {
     const int cb = t0 + c * kChunk;
 #pragma unroll
     for (int v = 0; v < NV; ++v) x[v] = load16_stream(row_off(cb, v, pool));
+  };
+  // both rows of chunk c, by the fast path where it applies
+  auto load_chunk = [&](Vec16 (&kx)[NV], Vec16 (&vx)[NV], int c) {
+    if (FAST && t0 + (c + 1) * kChunk <= t1) {
+      uint64_t toff[2];
+      chunk_tiles(c, toff);
+      load_tiles(kx, kbase, toff);
+      load_tiles(vx, vbase, toff);
+    } else {
+      load_rows(kx, P.kc, c);
+      load_rows(vx, P.vc, c);
+    }
   };
   // The chunk holding the new token: lanes at its row (and lanes past the
   // context, which re-read it) take the caller's K/V in pool format, staged
@@ -351,16 +432,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   // refilled with chunk nx's loads as soon as they are in LDS, so those loads
   // fly during the rest of the chunk.  One wave's LDS accesses complete in
   // order, so the V rows may overwrite the K rows once the K reads are issued.
+  //
+  // Only the partition's last chunk can run past its end.  Its rows past the
+  // end re-read the last token, so their scores repeat a real score and
+  // leave the chunk's max as it is; their weights are set to zero.
   auto process_chunk = [&](Vec16 (&kr)[NV], Vec16 (&vr)[NV], int c, int nx) {
     const int cb = t0 + c * kChunk;
+    const bool last = cb + kChunk > t1;
     const bool sub = c == new_chunk;  // wave-uniform, at most once
+    // the next chunk's loads: tile offsets once for K and V on the fast path
+    const bool nx_fast = FAST && nx < nchunks && t0 + (nx + 1) * kChunk <= t1;
+    uint64_t toff[2] = {0, 0};
+    if (nx_fast) chunk_tiles(nx, toff);
     if (sub) substitute(kr, 0, c);
     rows_to_lds(kr, L::swz_k);
-    if (nx < nchunks) load_rows(kr, P.kc, nx);
+    if (nx_fast) {
+      load_tiles(kr, kbase, toff);
+    } else if (nx < nchunks) {
+      load_rows(kr, P.kc, nx);
+    }
 
     // scores S^T (unscaled): lane (g, n) gets tokens 16 tau + 4 g + i of
     // head 16 ht + n
-    const bool last = cb + kChunk > t1;  // the partition's last chunk: tokens past its end are masked
     float sc[HT][8];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
@@ -375,17 +468,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
         for (int st = 0; st < NS; ++st) acc = mfma16x16x32(ka[st], q_operand(ht, st), acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[ht][4 * tau + i] = acc[i];
-        if (last) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (cb + 16 * tau + 4 * g + i >= t1) sc[ht][4 * tau + i] = -INFINITY;
-        }
       }
     }
 
     if (sub) substitute(vr, 1, c);
     rows_to_lds(vr, L::swz_v);
-    if (nx < nchunks) load_rows(vr, P.vc, nx);
+    if (nx_fast) {
+      load_tiles(vr, vbase, toff);
+    } else if (nx < nchunks) {
+      load_rows(vr, P.vc, nx);
+    }
 
     // online softmax per head column; the weights become the B operand.
     // The running max moves only when a chunk's max exceeds it by more than
@@ -393,22 +485,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
     // the accumulators is skipped by the whole wave in most chunks.  The
     // chunk's max is taken over unscaled scores and then scaled (rounding
     // is monotonic and sscale >= 0); each weight is 2^(score * sscale - m)
-    // with one rounding.
+    // with one rounding.  A column's max exceeds the bound exactly when one
+    // of its lanes' maxima does, so the max across the column's four lanes
+    // is taken only in chunks where some lane's does.
     half8_t pf[HT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      float mloc = sc[ht][0];
+      float mlane = sc[ht][0];
 #pragma unroll
-      for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sc[ht][j]);
-#if PA_GROUP_ROWMAX_SWAP
-      mloc = max_over_rows(mloc) * sscale;
-#else
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      mloc *= sscale;
-#endif
-      const bool raise = mloc > m[ht] + kLazy;  // uniform within a head column
-      if (__any(raise)) {
+      for (int j = 1; j < 8; ++j) mlane = fmaxf(mlane, sc[ht][j]);
+      if (__any(mlane * sscale > m[ht] + kLazy)) {
+        const float mloc = max_over_rows(mlane) * sscale;
+        const bool raise = mloc > m[ht] + kLazy;  // uniform within a head column
         const float m_new = raise ? mloc : m[ht];
         const float alpha = fast_exp2(m[ht] - m_new);  // 0 on the first chunk (m = -inf)
         lsum[ht] *= alpha;
@@ -426,7 +514,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
                             fast_exp2(fmaf(sc[ht][2 * k + 1], sscale, -m[ht]))};
         hp[k] = __builtin_convertvector(e, half2_t);
       }
-      if (last) {  // masked tokens weigh zero (also when sscale is 0)
+      if (last) {  // rows past the end weigh zero
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (cb + 16 * (j >> 2) + 4 * g + (j & 3) >= t1) hp[j >> 1][j & 1] = 0;
@@ -461,10 +549,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
 
   {
     Vec16 kr[NV], vr[NV];
-    if (w < nchunks) {
-      load_rows(kr, P.kc, w);
-      load_rows(vr, P.vc, w);
-    }
+    if (w < nchunks) load_chunk(kr, vr, w);
     for (int c = w; c < nchunks; c += NW) process_chunk(kr, vr, c, c + NW);
   }
   // the new token into its pool slot: the rows staged in LDS by the same
@@ -482,12 +567,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   // each head's weight sum over the wave's four lane groups
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) lsum[ht] = sum_over_rows(lsum[ht]);
+  __syncthreads();  // the exchange reuses the main loop's LDS
 
   // Merge the waves' partial results by head tile: tile t belongs to wave
   // t % NW.  In each round of XR tiles every other wave writes its state of
   // the round's tiles to LDS at once, and each owner merges the NW - 1 states
-  // of its tile in a fixed order (the waves after it, cyclically), so results
-  // are deterministic; every wave then stores the tiles it owns.  (A chain
+  // of each tile it owns in a fixed order (the waves after it, cyclically), so
+  // results are deterministic; every wave then stores the tiles it owns.  (A chain
   // of NW - 1 pairwise merges through one wave had each step move a whole
   // wave's state through LDS.)
   constexpr int NROUND = (HT + XR - 1) / XR;
@@ -635,6 +721,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   if (tid == 0) __hip_atomic_store(&P.counters[cidx], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// UNI addressing (wave-uniform tile bases): blocks of 16 or more tokens, and
+// a pool stride per block (all KV heads' tiles) that fits 32 bits.
+inline bool tile_addressing(const pa_kv_cache& c) {
+  const int kvb = c.kv_dtype == PA_F32 ? 4 : c.kv_dtype == PA_F16 ? 2 : 1;
+  return c.block_size >= 16 &&
+         static_cast<int64_t>(c.num_kv_heads) * c.block_size * c.head_dim * kvb <= static_cast<int64_t>(UINT32_MAX);
+}
+
 // Head tiles per workgroup: as many as the group needs, up to a register
 // budget that depends on head_dim.
 template <int D>
@@ -645,7 +739,7 @@ constexpr int max_head_tiles() {
 template <typename KV, int D, int HT>
 hipError_t launch_ht(const DecodeArgs& a, int groups) {
   constexpr int NW = PA_GROUP_WAVES;
-  auto kern = a.cache->block_size >= 16 ? decode_group_kernel<KV, D, HT, NW, true, false>
+  auto kern = tile_addressing(*a.cache) ? decode_group_kernel<KV, D, HT, NW, true, false>
                                         : decode_group_kernel<KV, D, HT, NW, false, false>;
   // Partition length: the shortest multiple of kPartitionTokens (doubling)
   // whose worst-case workgroup count fits the GPU's resident slots, so the
@@ -711,7 +805,7 @@ hipError_t launch_d(const DecodeArgs& a) {
 template <typename KV, int D, int HT>
 hipError_t launch_prefix_ht(const DecodeArgs& a) {
   constexpr int NW = PA_GROUP_WAVES;
-  auto kern = a.cache->block_size >= 16 ? decode_group_kernel<KV, D, HT, NW, true, true>
+  auto kern = tile_addressing(*a.cache) ? decode_group_kernel<KV, D, HT, NW, true, true>
                                         : decode_group_kernel<KV, D, HT, NW, false, true>;
   DecodeParams P = make_decode_params(a);
   const int G = a.num_q_heads / a.cache->num_kv_heads;
