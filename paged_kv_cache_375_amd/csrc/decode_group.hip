@@ -48,14 +48,27 @@
 namespace pa {
 namespace {
 
-#ifndef PA_GROUP_WAVES
-#define PA_GROUP_WAVES 4
-#endif
 // Minimum waves per SIMD the register allocation must allow: three where
 // the head tiles fit without spilling, else two.
 template <int D, int HT>
 constexpr int group_occupancy() {
   return D >= 128 || (D == 64 && HT >= 3) ? 2 : 3;
+}
+
+// Waves per workgroup.  With three or more head tiles a wave's state is
+// large (the five-tile instance holds 244 VGPRs), and so are a partial and
+// the waves' merge: eight waves, one workgroup per CU, take twice the tokens
+// per workgroup, so the launcher picks partitions twice as long and fewer
+// workgroups leave partials (Falcon-7B MQA layer 22.0 -> 20.4 us).  With
+// fewer tiles, four waves keep two or three workgroups per CU (the
+// Llama-2-70B layer takes 110 us with four, 172 us with eight).
+template <int HT>
+constexpr int group_waves() {
+#ifdef PA_GROUP_WAVES
+  return PA_GROUP_WAVES;
+#else
+  return HT >= 3 ? 8 : 4;
+#endif
 }
 
 constexpr int kLdsPerCu = 160 * 1024;  // gfx950
@@ -738,7 +751,7 @@ constexpr int max_head_tiles() {
 
 template <typename KV, int D, int HT>
 hipError_t launch_ht(const DecodeArgs& a, int groups) {
-  constexpr int NW = PA_GROUP_WAVES;
+  constexpr int NW = group_waves<HT>();
   auto kern = tile_addressing(*a.cache) ? decode_group_kernel<KV, D, HT, NW, true, false>
                                         : decode_group_kernel<KV, D, HT, NW, false, false>;
   // Partition length: the shortest multiple of kPartitionTokens (doubling)
@@ -804,7 +817,7 @@ hipError_t launch_d(const DecodeArgs& a) {
 // head, in tiles of 16 * HT.
 template <typename KV, int D, int HT>
 hipError_t launch_prefix_ht(const DecodeArgs& a) {
-  constexpr int NW = PA_GROUP_WAVES;
+  constexpr int NW = group_waves<HT>();
   auto kern = tile_addressing(*a.cache) ? decode_group_kernel<KV, D, HT, NW, true, true>
                                         : decode_group_kernel<KV, D, HT, NW, false, true>;
   DecodeParams P = make_decode_params(a);
