@@ -73,21 +73,23 @@ constexpr int group_waves() {
 
 constexpr int kLdsPerCu = 160 * 1024;  // gfx950
 
-// LDS arena of the grouped kernel (16-byte words): the main loop's K/V
-// chunks and q rows, later the waves' merge exchange, sized to the LDS that
-// each of the workgroups one CU holds at the kernel's occupancy may use.
+// LDS arena of the grouped kernel (16-byte words): the fold order's lengths,
+// then the main loop's K/V chunks, q rows and table slice, later the waves'
+// merge exchange, sized to the LDS that each of the workgroups one CU holds
+// at the kernel's occupancy may use.
 template <int D, int HT, int NW>
 struct GroupArena {
   static constexpr int LCH = D / 8, NDT = D / 16;
   static constexpr int kVbuf = NW * kChunk * LCH > kMergeCap / 2 ? NW * kChunk * LCH : kMergeCap / 2;
-  static constexpr int kLoop = kVbuf + HT * 16 * LCH;
+  static constexpr int kQs = HT * 16 * LCH;
+  static constexpr int kLoop = kVbuf + kQs + kTabEntries / 4;
+  static_assert(kVbuf * 4 >= kFoldMaxSeqs, "the fold order's lengths fit the K/V staging");
   static constexpr int exchange(int xr) { return xr * (NW - 1) * NDT * 64 + (xr * (NW - 1) * 64 + 1) / 2; }
   static constexpr int words(int xr) { return kLoop > exchange(xr) ? kLoop : exchange(xr); }
   // LDS per workgroup when the CU holds as many as the register occupancy
-  // allows, less what the kernel keeps beside the arena (table slice, new
-  // token rows, the fold order's lengths, flags)
-  static constexpr int kBudget = kLdsPerCu / (group_occupancy<D, HT>() * 4 / NW) - kTabEntries * 4 - 2 * D * 2 -
-                                  kFoldMaxSeqs * 4 - 1024;
+  // allows, less what the kernel keeps beside the arena (new token rows,
+  // flags) and some slack
+  static constexpr int kBudget = kLdsPerCu / (group_occupancy<D, HT>() * 4 / NW) - 2 * D * 2 - 512;
   static constexpr int pick(int xr) { return xr <= 1 || words(xr) * 16 <= kBudget ? xr : pick(xr - 1); }
   static constexpr int XR = pick(HT);
   static constexpr int kXo = XR * (NW - 1) * NDT * 64;
@@ -116,6 +118,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
+  // One LDS arena serves the phases in turn.  Set-up: the fold order's
+  // context lengths (at the start).  Set-up and main loop: each wave's K,
+  // then V, chunk as f16 rows (vbuf), the workgroup's q rows (qs, f16, zero
+  // past the group) and the partition's table slice (tab, part / block_size
+  // entries).  The waves' merge (see below): per round, the states of XR head
+  // tiles from the NW - 1 waves that do not own them (xo, xml: 16 and 8 bytes
+  // per lane).  The split-context merge: its scratch (at the start).  XR is
+  // as large as the LDS budget of the workgroups one CU holds allows, up to
+  // every tile in one round.
+  using A = GroupArena<D, HT, NW>;
+  constexpr int kVbuf = A::kVbuf, XR = A::XR;
+  static_assert(XR >= 1 && XR <= HT, "tiles per merge round");
+  __shared__ uint4 arena[A::kWords];
+  uint4* const vbuf = arena;
+  uint4* const qs = arena + kVbuf;
+  int* const tab = reinterpret_cast<int*>(arena + kVbuf + A::kQs);
+  float4_t(*const xo)[64] = reinterpret_cast<float4_t(*)[64]>(arena);
+  float2_t(*const xml)[64] = reinterpret_cast<float2_t(*)[64]>(arena + A::kXo);
   const int log2_bs = P.log2_bs;
   const int bs = 1 << log2_bs;
   int kvh, p, s, ctx, nparts, t0, t1, h0, nh, grp = 0;
@@ -154,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
       // y-th longest sequence in the first half and the y-th shortest in the
       // second, so each CU holds a long and a short one and all CUs finish
       // together.  Ranks order by length, then index (a permutation).
-      __shared__ int lens[kFoldMaxSeqs];
+      int* const lens = reinterpret_cast<int*>(vbuf);  // free until the main loop
       __shared__ int pick;
       const int B = P.num_seqs, half = (B + 1) / 2;
       const int want = s < half ? s : B - 1 - (s - half);
@@ -206,24 +226,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(group_o
   const int64_t head_rows = static_cast<int64_t>(kvh) * bs;  // token rows before head kvh in a block
   const int64_t block_rows = static_cast<int64_t>(P.hkv) * bs;
 
-  __shared__ int tab[kTabEntries];  // the partition's table slice (part / block_size entries)
   __shared__ int is_last;
   __shared__ Vec16 newkv[2][VCH];  // the new token's K and V rows in pool format
-  // One arena serves the phases in turn.  Set-up and main loop: each wave's
-  // K, then V, chunk as f16 rows (vbuf), then the workgroup's q rows (qs, f16,
-  // zero past the group).  The waves' merge (see below): per round, the
-  // states of XR head tiles from the NW - 1 waves that do not own them (xo,
-  // xml: 16 and 8 bytes per lane).  The split-context merge: its scratch
-  // (at the start).  XR is as large as the LDS budget of the workgroups one
-  // CU holds allows, up to every tile in one round.
-  using A = GroupArena<D, HT, NW>;
-  constexpr int kVbuf = A::kVbuf, XR = A::XR;
-  static_assert(XR >= 1 && XR <= HT, "tiles per merge round");
-  __shared__ uint4 arena[A::kWords];
-  uint4* const vbuf = arena;
-  uint4* const qs = arena + kVbuf;
-  float4_t(*const xo)[64] = reinterpret_cast<float4_t(*)[64]>(arena);
-  float2_t(*const xml)[64] = reinterpret_cast<float2_t(*)[64]>(arena + A::kXo);
 
   // Fused append: every workgroup reading the new token takes it from the
   // caller's rows (staged in LDS in pool format) instead of the pool, and the
