@@ -6,8 +6,9 @@
 // One workgroup per (KV head and group of up to 16 * HT query heads,
 // partition, sequence).  The partition length is chosen per launch (a
 // multiple of kPartitionTokens): the shortest whose workgroups all fit on the
-// GPU at once, else kPartitionTokens.  Its NW wavefronts take
-// 32-token chunks of the partition in turn; a chunk is processed as
+// GPU at once, else kPartitionTokens.  Its NW wavefronts (4, or 8 at three
+// or more head tiles) take 32-token chunks of the partition in turn; a chunk
+// is processed as
 //
 //   S^T[32 tokens][16 heads] = K[32][D] . Q^T[D][16]      (2 x D/32 MFMAs per head tile)
 //   online softmax of each head's column (scores in log2 units, exp2)
@@ -32,9 +33,10 @@
 // loads are issued as soon as the current ones are in LDS.
 //
 // Heads past the group (padding up to 16 per tile) have q = 0 and are never
-// written.  The NW wavefronts' partial results are merged in a fixed order
-// through LDS, and partitions by the last workgroup to finish, exactly as in
-// the per-head kernel (same workspace layout), so results are deterministic.
+// written.  The NW wavefronts' partial results are merged per head tile in a
+// fixed order through LDS, and partitions by the last workgroup to finish,
+// with the rescaling of the per-head kernel's merge launch (same workspace
+// layout), so results are deterministic.
 // Blocks are fetched through the table in logical order and need not be
 // adjacent [F55 §块表]; [IPX §分离逻辑顺序与实际存储位置].
 #include <hip/hip_runtime.h>
