@@ -58,10 +58,10 @@ constexpr int group_occupancy() {
 }
 
 // Waves per workgroup.  With three or more head tiles a wave's state is
-// large (the five-tile instance holds 244 VGPRs), and so are a partial and
+// large (the five-tile instance holds about 240 VGPRs), and so are a partial and
 // the waves' merge: eight waves, one workgroup per CU, take twice the tokens
 // per workgroup, so the launcher picks partitions twice as long and fewer
-// workgroups leave partials (Falcon-7B MQA layer 22.0 -> 20.4 us).  With
+// workgroups leave partials (Falcon-7B MQA layer 22.0 -> 20.5 us).  With
 // fewer tiles, four waves keep two or three workgroups per CU (the
 // Llama-2-70B layer takes 110 us with four, 172 us with eight).
 template <int HT>
