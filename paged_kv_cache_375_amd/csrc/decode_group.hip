@@ -57,20 +57,13 @@ constexpr int group_occupancy() {
   return D >= 128 || (D == 64 && HT >= 3) ? 2 : 3;
 }
 
-// Waves per workgroup.  With three or more head tiles a wave's state is
-// large (the five-tile instance holds about 240 VGPRs), and so are a partial and
-// the waves' merge: eight waves, one workgroup per CU, take twice the tokens
-// per workgroup, so the launcher picks partitions twice as long and fewer
-// workgroups leave partials (Falcon-7B MQA layer 22.0 -> 20.5 us).  With
-// fewer tiles, four waves keep two or three workgroups per CU (the
-// Llama-2-70B layer takes 110 us with four, 172 us with eight).
+// Waves per workgroup of the prefix pass: eight with three or more head
+// tiles (a wave's state is then large, about 240 VGPRs at five tiles, and
+// eight waves fill a CU), else four.  The decode launch chooses per launch
+// (launch_ht).
 template <int HT>
 constexpr int group_waves() {
-#ifdef PA_GROUP_WAVES
-  return PA_GROUP_WAVES;
-#else
   return HT >= 3 ? 8 : 4;
-#endif
 }
 
 constexpr int kLdsPerCu = 160 * 1024;  // gfx950
@@ -755,29 +748,29 @@ constexpr int max_head_tiles() {
   return D >= 128 ? 2 : 5;
 }
 
-template <typename KV, int D, int HT>
-hipError_t launch_ht(const DecodeArgs& a, int groups) {
-  constexpr int NW = group_waves<HT>();
-  auto kern = tile_addressing(*a.cache) ? decode_group_kernel<KV, D, HT, NW, true, false>
-                                        : decode_group_kernel<KV, D, HT, NW, false, false>;
-  // Partition length: the shortest multiple of kPartitionTokens (doubling)
-  // whose worst-case workgroup count fits the GPU's resident slots, so the
-  // whole launch runs as one round; when even one partition per unit does
-  // not fit, many short partitions balance best.  Bounded by the LDS table
-  // slice (kTabEntries entries).
-  const int64_t units = static_cast<int64_t>(a.cache->num_kv_heads) * groups * a.num_seqs;
-  const int slots = resident_slots(reinterpret_cast<const void*>(kern), NW * 64);
-  const int64_t cap = static_cast<int64_t>(kTabEntries) * a.cache->block_size;
-  const int64_t span = a.max_ctx - a.min_begin;  // the longest run of a sequence's own tokens
-  int part = kPartitionTokens;
+// The shortest partition length (a multiple of kPartitionTokens, doubling,
+// up to the table slice's kTabEntries blocks) whose worst-case workgroup
+// count fits `slots` resident workgroups, so that the launch runs as one
+// round; 0 if none does.
+inline int one_round_part(int64_t units, int slots, int64_t span, int64_t cap) {
   for (int64_t pp = kPartitionTokens; pp <= cap; pp *= 2) {
     const int64_t parts = (span + pp - 1) / pp;
-    if (units * (parts > 0 ? parts : 1) <= slots) {
-      part = static_cast<int>(pp);
-      break;
-    }
+    if (units * (parts > 0 ? parts : 1) <= slots) return static_cast<int>(pp);
     if (pp >= span) break;
   }
+  return 0;
+}
+
+using GroupKernel = void (*)(const DecodeParams, int);
+
+template <typename KV, int D, int HT, int NW>
+GroupKernel group_kernel(const pa_kv_cache& c) {
+  return tile_addressing(c) ? decode_group_kernel<KV, D, HT, NW, true, false>
+                            : decode_group_kernel<KV, D, HT, NW, false, false>;
+}
+
+template <int NW>
+hipError_t launch_group(const DecodeArgs& a, int groups, GroupKernel kern, int part, int slots, int64_t units) {
   DecodeParams P = make_decode_params(a);
   P.part_tokens = part;
   const int grid_parts = decode_grid_parts(a, part);
@@ -796,6 +789,32 @@ hipError_t launch_ht(const DecodeArgs& a, int groups) {
   const hipError_t e = hipGetLastError();
   if (a.ev[1]) (void)hipEventRecord(a.ev[1], a.stream);
   return e;
+}
+
+// Waves per workgroup and partition length, per launch.  A launch runs as
+// one round if it can: partitions as short as the GPU's resident slots
+// allow (see one_round_part).  Eight-wave workgroups hold a CU alone (the
+// accumulators leave room for no second one), so where an eight-wave launch
+// fits in one round its partitions are at least twice as long as a
+// four-wave launch's would be: fewer workgroups leave partials and each is
+// served by twice the waves (Falcon-7B MQA layer 20.0 against 22.0 us, the
+// Llama-2-70B layer's share under tensor parallelism over 8 GPUs 22.9
+// against 24.6 us).  Where it does not fit (the whole Llama-2-70B layer:
+// 512 units, one 4,096-token partition each on four-wave workgroups, two
+// per CU), four waves; when even those need several rounds, 512-token
+// partitions balance best.
+template <typename KV, int D, int HT>
+hipError_t launch_ht(const DecodeArgs& a, int groups) {
+  const int64_t units = static_cast<int64_t>(a.cache->num_kv_heads) * groups * a.num_seqs;
+  const int64_t cap = static_cast<int64_t>(kTabEntries) * a.cache->block_size;
+  const int64_t span = a.max_ctx - a.min_begin;  // the longest run of a sequence's own tokens
+  const GroupKernel k8 = group_kernel<KV, D, HT, 8>(*a.cache);
+  const int s8 = resident_slots(reinterpret_cast<const void*>(k8), 8 * 64);
+  if (const int p8 = one_round_part(units, s8, span, cap)) return launch_group<8>(a, groups, k8, p8, s8, units);
+  const GroupKernel k4 = group_kernel<KV, D, HT, 4>(*a.cache);
+  const int s4 = resident_slots(reinterpret_cast<const void*>(k4), 4 * 64);
+  const int p4 = one_round_part(units, s4, span, cap);
+  return launch_group<4>(a, groups, k4, p4 ? p4 : kPartitionTokens, s4, units);
 }
 
 template <typename KV, int D>
