@@ -76,6 +76,43 @@ def test_group_kernel_long_partitions():
     assert err <= TOL["f16"]
 
 
+# Launches with so many (KV head, query group, sequence) units that eight-wave
+# workgroups (one per CU, at most two per CU at any register count) cannot
+# run them in one round, so the launcher takes four-wave workgroups; with at
+# least 2,048 units even those need several rounds, so partitions are 512
+# tokens and longer contexts merge in the launch.
+# (q heads, kv heads, head_dim, pool dtype, block size, sequences)
+FOUR_WAVE_CASES = [
+    (16, 8, 128, "f16", 16, 256),    # G 2, head_dim 128
+    (64, 32, 64, "f16", 16, 64),     # G 2, head_dim 64
+    (48, 16, 32, "f16", 4, 128),     # G 3, head_dim 32, 4-token blocks (per-row addressing)
+    (64, 16, 128, "e4m3", 16, 128),  # FP8 pool, head_dim 128
+    (40, 8, 64, "e4m3", 8, 256),     # FP8 pool, head_dim 64, 8-token blocks
+    (68, 2, 128, "f16", 16, 512),    # G 34: two tiles over two workgroups per KV head
+    (71, 1, 64, "f16", 16, 2048),    # G 71: five tiles
+]
+
+
+@pytest.mark.parametrize("case", FOUR_WAVE_CASES, ids=lambda c: "q{}_kv{}_d{}_{}_bs{}_B{}".format(*c))
+def test_group_kernel_four_wave_launches(case):
+    hq, hkv, d, kv, bs, b = case
+    tiles = -(-(hq // hkv) // 16)               # 16-head tiles per KV head
+    groups = -(-tiles // (2 if d >= 128 else 5))  # workgroups per KV head (2 or 5 tiles each at most)
+    assert hkv * groups * b >= 2048
+    wl = Workload(f"group4w_{hq}x{hkv}x{d}_{kv}_bs{bs}_B{b}", hq, hkv, d, bs, b, 1, 700, kv=kv)
+    print(f"[group4w] {wl}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    out = out_f64(gpu.run())
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    want = ref.decode_threaded()
+    err = float(np.max(np.abs(out - want)))
+    print(f"[group4w] {wl.name}: max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]
+
+
 def test_group_kernel_placement_invariance_bit_exact():
     wl = _wl(64, 8, 128, "f16", 16)
     dr, gpu, ref = build_pair(wl)
