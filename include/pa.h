@@ -462,10 +462,10 @@ pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches) PA_NOEXCEP
  * table in logical order [F55 §块表] (entries outside [0, num_blocks) make
  * that sequence read nothing).  mode 1 reads both whole pools from start to
  * end, each workgroup one contiguous span (tables and lengths are ignored).
- * Each lane folds its loaded words with XOR and writes sink (device, uint32
- * [1024], caller-owned) only if the fold equals a fixed value, so the loads
- * cannot be dropped; the sink's contents mean nothing.  Asynchronous on
- * stream.
+ * Each lane folds its loaded words with XOR and writes its fold to one word
+ * of sink (device, uint32 [1024], caller-owned) only if the fold equals
+ * 0x9E3779B9, so the loads cannot be dropped; sink words are left as they
+ * were or set to that value, and mean nothing.  Asynchronous on stream.
  */
 pa_status pa_read_probe(const pa_kv_cache* cache, const int32_t* block_tables, const int32_t* context_lens,
                         int32_t num_seqs, int32_t max_blocks_per_seq, int32_t max_context_len, int32_t mode,
