@@ -311,7 +311,7 @@ def main():
         print(f"bench.py needs --steps >= 1 and --warmup >= 0; got {args.steps}, {args.warmup}", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
 

@@ -455,7 +455,7 @@ pa_status pa_timing_read(double* decode_ms, int32_t* decode_launches) PA_NOEXCEP
 /*
  * pa_read_probe — measurement only: the rate at which this GPU reads the
  * pools, without any of the decode's arithmetic, so that the decode kernels
- * can be judged against what their access pattern allows.  mode 0 runs the
+ * can be compared with what their access pattern allows.  mode 0 runs the
  * per-head decode kernel with its arithmetic compiled out, treating every KV
  * head as one query head: the same grid, table staging and 16-byte
  * non-temporal K and V loads, every sequence's rows read through its block
