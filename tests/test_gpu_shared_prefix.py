@@ -107,3 +107,44 @@ def test_full_prefix_workload_parity():
     assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
     assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
     full_size_check(wl.name + " (shared-prefix path)", wl, out, ref, dr)
+
+
+def random_prefix_workload(i):
+    rng = np.random.default_rng(2000 + i)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 5, 8, 16, 40, 71]))
+    if i % 6 == 0:
+        g = 1  # multi-head attention: the per-head decode after the prefix pass
+    d = int(rng.choice([32, 64, 128]))
+    bs = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    kv = str(rng.choice(["f16", "e4m3"]))
+    hq = hkv * g
+    prefix = int(rng.integers(bs, 1501))  # may end inside a block
+    hi = int(rng.integers(1, 1501))
+    lo = int(rng.integers(1, hi + 1))
+    per_seq = hq * (prefix + (lo + hi) / 2)
+    b = int(rng.integers(2, int(max(2, min(40, 2e6 // per_seq))) + 1))
+    return Workload(f"sprand{i}_q{hq}_kv{hkv}_d{d}_bs{bs}_{kv}_B{b}_p{prefix}_ctx{lo}-{hi}", hq, hkv, d, bs, b, lo, hi,
+                    kv=kv, prefix_len=prefix)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_shared_prefix_parity(i):
+    """Seeded random shapes through pa_decode_shared_prefix (one group over
+    the whole batch, sharing the prefix's whole blocks), with the append
+    fused: the per-head or grouped decode after the prefix pass, at block
+    sizes 1 to 64 and prefixes that end on or inside a block."""
+    wl = random_prefix_workload(i)
+    print(f"[shared-prefix] {wl.name}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    shared = _shared_blocks(wl)
+    t = gpu.scenario.tables
+    assert (t[:, :shared] == t[0, :shared]).all()
+    out = out_f64(_run(gpu, [0, wl.batch], [shared], True))
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    err = float(np.max(np.abs(out - ref.decode_threaded())))
+    print(f"[shared-prefix] {wl.name}: max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]
