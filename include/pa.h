@@ -199,7 +199,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  * multi-query attention share one KV head among contiguous query heads
  * [F55 §后来的做法]).  q, out: device [num_seqs][num_q_heads][head_dim] of
  * dtype act; fp32 accumulation; the output is rounded to act (nearest even).
- * Contexts longer than one 512-token partition are split; the partitions'
+ * Contexts longer than one partition are split (512 tokens for the per-head
+ * kernel; for the grouped kernel a multiple of 512 chosen per launch, so
+ * that its workgroups fit the GPU at once where they can); the partitions'
  * (max, sum, vector) partial results are merged exactly (the online softmax
  * gives the same result [F55 related plate F51]): by a second, small launch
  * on the same stream for the per-head kernel (MHA, and f32 activations),
