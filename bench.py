@@ -45,15 +45,24 @@ def workload_label(wl):
 def decode_kernel_name(wl, shared=False):
     """The decode kernel that serves the workload (matrix cores when query
     heads share KV heads and activations are f16, else the per-head kernel
-    and its merge launch), after the prefix pass when a shared prefix takes
-    the shared-prefix path."""
-    if wl.num_q_heads > wl.num_kv_heads and wl.act == "f16":
+    and its merge launch), with the prefix pass when a shared prefix takes
+    the shared-prefix path: in the same launch as a per-head decode over an
+    FP8 pool with blocks of at least 16 tokens (and a wave load's tokens),
+    else a launch of its own before the decode."""
+    grouped = wl.num_q_heads > wl.num_kv_heads and wl.act == "f16"
+    if grouped:
         k = "decode_group_kernel (grouped heads on MFMA: append + split-context attention + merge)"
     else:
         k = "decode_kernel (per head on VALU: append + split-context attention) + merge_kernel (split-context merge)"
-    if shared:
-        k = "prefix pass (decode_group_kernel: the shared blocks once per KV head for every sequence, MFMA) + " + k
-    return k
+    if not shared:
+        return k
+    pass_ = "the shared blocks once per KV head for every sequence, MFMA"
+    per_load = 64 // (wl.head_dim // 16)  # tokens of one wave load of the FP8 per-head kernel
+    if (not grouped and wl.act == "f16" and wl.kv == "e4m3" and wl.head_dim in (32, 64, 128)
+            and wl.block_size >= max(16, per_load)):
+        return ("decode_prefix_fused_kernel (per head on VALU: append + split-context attention; then, in the "
+                f"launch's last workgroups, the prefix pass: {pass_}) + merge_kernel (split-context merge)")
+    return f"prefix pass (decode_group_kernel: {pass_}) + " + k
 
 
 def kernel_source_hash():

@@ -281,10 +281,17 @@ pa_status pa_decode_step_noalloc(const pa_kv_cache* cache, const void* q, const 
  * group_shared_blocks[g] (host int32) table entries.  A prefix pass reads
  * those blocks once per KV head, through the table of the group's first
  * sequence, for all of the group's (sequence, query head) rows on the matrix
- * cores, and leaves per-row partials; the decode launch then covers each
- * sequence's own tokens and merges both exactly.  The caller guarantees the
- * sharing: entries past the first sequence's are not read for the shared
- * range.  A sequence whose context is shorter than its group's shared
+ * cores, and leaves per-row partials; the decode covers each sequence's own
+ * tokens, and both are merged exactly.  The grouped decode runs after the
+ * prefix pass and starts from its partials.  The per-head decode over an
+ * FP8 pool with blocks of at least 16 tokens (and of at least
+ * 64 / (head_dim / 16)) runs in the same launch as the prefix pass, whose
+ * workgroups come last, and a merge launch follows; the slot of a token
+ * appended by that launch must not lie in a shared block, which copy on
+ * write guarantees (pa_seq_append_slot never leaves a shared block as the
+ * write target).  Otherwise the prefix pass, the per-head decode and the
+ * merge are three launches.  The caller guarantees the sharing: entries
+ * past the first sequence's are not read for the shared range.  A sequence whose context is shorter than its group's shared
  * tokens, or (when appending) whose new token would fall inside them, gets
  * NaN output.  At most 16 groups; sequences outside every group decode
  * normally.  Needs f16 activations and an f16 or FP8 pool when any group

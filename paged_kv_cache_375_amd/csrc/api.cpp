@@ -287,15 +287,21 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
   }
   hipError_t e = hipSuccess;
   if (a.ngroups > 0) {
-    // The prefix pass first, then the decode launch, on the caller's stream:
-    // the decode's first partition of each head starts from the prefix's
-    // partials.  (A prefix pass beside the decode on a second stream, the two
-    // meeting at per-row arrival counters, was slower: its workgroups waited
-    // for slots the decode's kept refilling.)  The timing events bracket both.
+    // Where the decode runs on the per-head kernel's two-wave workgroups (FP8
+    // pools), the prefix pass shares its launch and a merge launch follows.
+    // Otherwise the prefix pass comes first, then the decode launch, on the
+    // caller's stream: the grouped decode's first partition of each head
+    // starts from the prefix's partials.  (A prefix pass beside the decode on
+    // a second stream was slower: its workgroups waited for slots the
+    // decode's kept refilling.)  The timing events bracket everything.
     if (a.ev[0]) (void)hipEventRecord(a.ev[0], a.stream);
     a.ev[0] = nullptr;
-    e = pa::launch_prefix_pass(a);
-    if (e == hipSuccess) e = pa::launch_decode(a);
+    if (pa::prefix_fused_applies(a)) {
+      e = pa::launch_decode_prefix_fused(a);
+    } else {
+      e = pa::launch_prefix_pass(a);
+      if (e == hipSuccess) e = pa::launch_decode(a);
+    }
   } else {
     e = pa::launch_decode(a);
   }

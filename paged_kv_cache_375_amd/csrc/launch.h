@@ -42,7 +42,10 @@ hipError_t launch_read_probe(const pa_kv_cache& c, const int32_t* tables, const 
 // per call; the prefix pass splits each prefix into partitions of
 // kPrefixPartTokens tokens.
 constexpr int kMaxPrefixGroups = 16;
-constexpr int kPrefixPartTokens = 256;
+#ifndef PA_PREFIX_PART_TOKENS
+#define PA_PREFIX_PART_TOKENS 256
+#endif
+constexpr int kPrefixPartTokens = PA_PREFIX_PART_TOKENS;
 
 struct DecodeArgs {
   const pa_kv_cache* cache;
@@ -105,5 +108,11 @@ hipError_t launch_decode_group(const DecodeArgs& a);
 // pools): every group's shared tokens, read once per KV head for all of the
 // group's query rows, leave partials in the workspace.
 hipError_t launch_prefix_pass(const DecodeArgs& a);
+// A shared-prefix decode whose decode runs on the per-head kernel's two-wave
+// workgroups (f16 activations, FP8 pools, one query head per KV head, blocks
+// of 16 or more tokens): the prefix pass and the decode in one launch, then
+// the merge launch.
+bool prefix_fused_applies(const DecodeArgs& a);
+hipError_t launch_decode_prefix_fused(const DecodeArgs& a);
 
 }  // namespace pa

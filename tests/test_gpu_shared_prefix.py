@@ -6,7 +6,7 @@ Sequences that fork one prompt hold its full blocks in common [F55 ¬ßÂ∏∏ËßÅÈóÆÈ¢
 blocks once per KV head for all of a group's query rows, then each sequence's
 own tokens, and merges both; the output must be the same attention as over
 each whole context.  Cases cover FP8 and f16 pools, MHA, GQA and MQA, head
-sizes 32 to 128, block sizes 1 to 16, prefixes that end on and inside a block
+sizes 32 to 128, block sizes 1 to 64, prefixes that end on and inside a block
 (the partial block is each sequence's own copy after copy-on-write), fused
 and separate append, several groups, sequences outside every group, and a
 group whose claim does not hold.
@@ -28,6 +28,13 @@ CASES = [
     Workload("sp_f16_mqa", 71, 1, 64, 16, 4, 1, 600, prefix_len=300),
     Workload("sp_f16_mha_bs4", 8, 8, 64, 4, 5, 1, 800, prefix_len=257),
     Workload("sp_fp8_gqa_d32_bs1", 12, 3, 32, 1, 5, 1, 400, kv="e4m3", prefix_len=130),
+    # FP8 multi-head attention runs the prefix pass inside the decode launch
+    # where blocks hold a wave load's tokens and at least 16 (head sizes 64
+    # and 32 here), and before it otherwise (8- and 16-token blocks below)
+    Workload("sp_fp8_mha_d64_bs32", 16, 16, 64, 32, 5, 1, 700, kv="e4m3", prefix_len=320),
+    Workload("sp_fp8_mha_d32_bs64", 8, 8, 32, 64, 5, 1, 900, kv="e4m3", prefix_len=640),
+    Workload("sp_fp8_mha_bs8", 8, 8, 128, 8, 5, 1, 600, kv="e4m3", prefix_len=200),
+    Workload("sp_fp8_mha_d32_bs16", 8, 8, 32, 16, 5, 1, 600, kv="e4m3", prefix_len=256),
 ]
 
 
@@ -78,8 +85,10 @@ def test_shared_prefix_groups_and_outsiders():
     assert err <= TOL["e4m3"]
 
 
-def test_shared_prefix_claim_past_a_context_gives_nan_for_that_sequence_only():
-    wl = Workload("sp_claim", 8, 8, 64, 16, 4, 1, 200, prefix_len=64)
+@pytest.mark.parametrize("kv", ["f16", "e4m3"])
+def test_shared_prefix_claim_past_a_context_gives_nan_for_that_sequence_only(kv):
+    wl = Workload("sp_claim", 8, 8, 64, 16, 4, 1, 200, kv=kv, prefix_len=64)
+    print(f"[shared-prefix] {wl}", flush=True)
     dr, gpu, ref = build_pair(wl)
     short = int(np.argmin(dr.ctx))
     claim = (int(dr.ctx[short]) + 15) // 16  # covers the new token's slot: not a shared range
@@ -91,7 +100,7 @@ def test_shared_prefix_claim_past_a_context_gives_nan_for_that_sequence_only():
     ref.append()
     want = ref.decode()[order]
     assert np.isnan(out[0]).all()
-    assert float(np.max(np.abs(out[1:] - want[1:]))) <= TOL["f16"]
+    assert float(np.max(np.abs(out[1:] - want[1:]))) <= TOL[kv]
 
 
 def test_full_prefix_workload_parity():
@@ -132,7 +141,8 @@ def random_prefix_workload(i):
 def test_random_shared_prefix_parity(i):
     """Seeded random shapes through pa_decode_shared_prefix (one group over
     the whole batch, sharing the prefix's whole blocks), with the append
-    fused: the per-head or grouped decode after the prefix pass, at block
+    fused: the per-head decode beside or after the prefix pass, or the
+    grouped decode after it, at block
     sizes 1 to 64 and prefixes that end on or inside a block."""
     wl = random_prefix_workload(i)
     print(f"[shared-prefix] {wl.name}", flush=True)
