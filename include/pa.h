@@ -212,13 +212,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  * (1024 partitions; larger values return PA_ERR_UNSUPPORTED); workspace must hold
  * pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len)
  * bytes (NULL allowed when that size is 0).  The workspace must be
- * zero-filled before its first use: its arrival counters (the first
- * num_seqs * num_q_heads int32, padded to 256 bytes) must start at zero, and
- * every completed call leaves them at zero again, so a workspace can be
- * reused call after call with the same num_seqs and num_q_heads (any
- * max_context_len it is large enough for); calls with other sizes need a
- * workspace zero-filled for them.  Calls that overlap in time must not share
- * a workspace.  A context length of 0 yields zeros.  A
+ * zero-filled before its first use.  It begins with the arrival counters,
+ * one int32 per (sequence, query head) row, in a region sized by
+ * workspace_bytes for the most rows such a workspace could serve; the
+ * partials follow it.  Every completed call leaves its counters at zero, so
+ * a workspace can be reused call after call with any sizes it is large
+ * enough for (batches that grow and shrink included), provided every call on
+ * it passes the same workspace_bytes.  Calls that overlap in time must not
+ * share a workspace.  A context length of 0 yields zeros.  A
  * sequence whose context exceeds max_context_len or
  * max_blocks_per_seq * block_size, or whose table holds a block id outside
  * [0, num_blocks), yields NaN for every head (and reads nothing out of range).
@@ -298,7 +299,7 @@ pa_status pa_decode_step_noalloc(const pa_kv_cache* cache, const void* q, const 
  * shares blocks (else PA_ERR_UNSUPPORTED).  Workspace: at least
  * pa_decode_shared_workspace_size(num_seqs, num_q_heads, head_dim,
  * max_context_len, the largest group_shared_blocks * block_size) bytes,
- * zero-filled before first use (the counters are left at zero).
+ * zero-filled before first use and reusable as pa_decode's.
  */
 pa_status pa_decode_shared_prefix(const pa_kv_cache* cache, const void* q, const void* k_new, const void* v_new,
                                   void* out, int32_t act, int32_t num_q_heads, const int32_t* block_tables,

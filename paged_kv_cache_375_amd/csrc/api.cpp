@@ -136,15 +136,34 @@ extern "C" pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void
 
 // Workspace: arrival counters [num_seqs][num_q_heads] int32 (padded to 256
 // bytes), then (max, sum) pairs and unnormalised vectors per partition.
-static size_t counters_bytes(int32_t num_seqs, int32_t num_q_heads) {
-  const size_t b = static_cast<size_t>(num_seqs) * num_q_heads * sizeof(int32_t);
+// A workspace starts with the arrival counters (one int32 per (sequence,
+// query head) row), then the partials ((max, sum) and head_dim floats per row
+// and partition).  The counters' region is sized by the workspace itself,
+// for the most rows any call could use it for: a row that needs a workspace
+// takes its counter and at least two partials of head_dim + 2 >= 34 floats
+// (kMinRowBytes).  So on one workspace the counters of every call lie below
+// the partials of every call, whatever their batch: each call leaves its
+// counters at zero, and no call's partials land on a later call's counters.
+constexpr size_t kMinRowBytes = sizeof(int32_t) + 2 * (32 + 2) * sizeof(float);
+
+static size_t counters_region(size_t workspace_bytes) {
+  const size_t b = workspace_bytes / kMinRowBytes * sizeof(int32_t);
   return (b + 255) & ~static_cast<size_t>(255);
 }
 
+static size_t partials_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t parts) {
+  return static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+}
+
+// The least size W whose room past counters_region(W) holds the partials
+// with 256 bytes to spare, so that every larger size holds them too (the
+// region grows 256 bytes at a time, once per 64 * kMinRowBytes bytes of W):
+// W >= (partials + 512) * kMinRowBytes / (kMinRowBytes - 4) leaves W -
+// counters_region(W) >= W (1 - 4 / kMinRowBytes) - 255 >= partials + 257.
 static size_t workspace_bytes_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t parts) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || parts <= 1) return 0;
-  return counters_bytes(num_seqs, num_q_heads) +
-         static_cast<size_t>(num_seqs) * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+  const size_t t = partials_bytes(num_seqs, num_q_heads, head_dim, parts) + 512;
+  return (t * kMinRowBytes + (kMinRowBytes - sizeof(int32_t)) - 1) / (kMinRowBytes - sizeof(int32_t));
 }
 
 // Partials per (sequence, head) of a shared-prefix decode: the prefix pass's
@@ -238,7 +257,11 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
     return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL device pointer", fn);
   const int32_t parts = max_shared > 0 ? shared_parts_for(max_context_len, max_shared) : max_parts_for(max_context_len);
   const size_t need = workspace_bytes_for(num_seqs, num_q_heads, cache->head_dim, parts);
-  if (workspace_bytes < need || (need > 0 && !workspace))
+  // (the size suffices for the layout; both conditions are checked as well)
+  if (need > 0 && (!workspace || workspace_bytes < need ||
+                   counters_region(workspace_bytes) < static_cast<size_t>(num_seqs) * num_q_heads * sizeof(int32_t) ||
+                   workspace_bytes - counters_region(workspace_bytes) <
+                       partials_bytes(num_seqs, num_q_heads, cache->head_dim, parts)))
     return fail(PA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, need);
 
   pa::DecodeArgs a{};
@@ -276,7 +299,7 @@ pa_status decode_common(const char* fn, const pa_kv_cache* cache, const void* q,
   if (need > 0) {
     char* base = static_cast<char*>(workspace);
     a.counters = reinterpret_cast<int*>(base);
-    a.ws_ml = reinterpret_cast<float*>(base + counters_bytes(num_seqs, num_q_heads));
+    a.ws_ml = reinterpret_cast<float*>(base + counters_region(workspace_bytes));
     a.ws_o = a.ws_ml + static_cast<size_t>(num_seqs) * num_q_heads * a.max_parts * 2;
   }
   a.stream = static_cast<hipStream_t>(stream);

@@ -64,6 +64,30 @@ def test_noalloc_refuses_more_scratch_than_it_holds_before_any_device_call():
     assert b"32" in _lib.lib().pa_last_error() or b"33554432" in _lib.lib().pa_last_error()
 
 
+def _counters_region(w):
+    """The arrival counters' share of a w-byte workspace: one int32 for each
+    of the most rows w could serve (a counter and two partials of 34 floats,
+    276 bytes, per row), in 256-byte units; the partials follow it."""
+    return (w // 276 * 4 + 255) // 256 * 256
+
+
+def _check_workspace_layout(need, rows, partials):
+    # the workspace size leaves room for every row's counter and for the
+    # partials past the counters, and so does every larger size (calls that
+    # share one buffer pass its size, so they share one counter region)
+    for w in list(range(need, need + 40000, 7)) + [need * 3, need * 1000 + 123]:
+        assert _counters_region(w) >= 4 * rows
+        assert w - _counters_region(w) >= partials
+
+
+def test_workspace_size_leaves_every_call_its_counters_below_the_partials():
+    L = _lib.lib()
+    for B, hq, d, ctx in [(1, 1, 32, 513), (2, 4, 128, 2048), (30, 40, 128, 2048), (128, 71, 64, 2048),
+                          (64, 64, 128, 4096), (256, 128, 128, 524288), (3, 8, 64, 1025)]:
+        parts = (ctx + 511) // 512
+        _check_workspace_layout(L.pa_decode_workspace_size(B, hq, d, ctx), B * hq, B * hq * parts * (d + 2) * 4)
+
+
 def test_decode_argument_checks_fail_before_any_launch():
     L = _lib.lib()
     assert _decode(_cache(block_size=3)) == _lib.PA_ERR_UNSUPPORTED
@@ -74,7 +98,7 @@ def test_decode_argument_checks_fail_before_any_launch():
     assert _decode(_cache(kv_dtype=_lib.PA_FP8_E4M3, k_scale=0.0)) == _lib.PA_ERR_INVALID_ARGUMENT
     # long contexts need the split-context workspace
     need = L.pa_decode_workspace_size(2, 4, 128, 2048)
-    assert need == 256 + 2 * 4 * 4 * (128 + 2) * 4  # counters, then 512-token partitions
+    _check_workspace_layout(need, rows=2 * 4, partials=2 * 4 * 4 * (128 + 2) * 4)  # 512-token partitions
     assert _decode(_cache(), mctx=2048, wsb=need - 1, ws=0x7000) == _lib.PA_ERR_WORKSPACE_TOO_SMALL
     assert b"workspace" in L.pa_last_error()
     assert L.pa_decode_workspace_size(2, 4, 128, 512) == 0  # one partition: no workspace
@@ -348,7 +372,7 @@ def test_shared_prefix_argument_checks_fail_before_any_launch():
     assert _shared(c, [0, 0, 0], [2, 1], B=0) == _lib.PA_OK
     # workspace: prefix partials (256 tokens each) plus the decode's (512 each)
     need = L.pa_decode_shared_workspace_size(3, 4, 128, 1000, 300)
-    assert need == 256 + 3 * 4 * (2 + 2) * (128 + 2) * 4
+    _check_workspace_layout(need, rows=3 * 4, partials=3 * 4 * (2 + 2) * (128 + 2) * 4)
     assert L.pa_decode_shared_workspace_size(3, 4, 128, 1000, 0) == L.pa_decode_workspace_size(3, 4, 128, 1000)
     assert _shared(c, [0, 3], [19], mctx=1000, mb=64, wsb=need - 1) == _lib.PA_ERR_WORKSPACE_TOO_SMALL  # 304 tokens
     # no group shares anything: the plain decode's rules (f32 allowed)

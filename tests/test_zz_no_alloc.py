@@ -78,3 +78,28 @@ def test_noalloc_refuses_more_scratch_than_it_holds():
                                 out=torch.empty_like(gpu.q))
     assert e.value.status == _lib.PA_ERR_WORKSPACE_TOO_SMALL
     assert "32" in str(e.value) or "33554432" in str(e.value)
+
+
+@pytest.mark.parametrize("wl", CASES[:2], ids=lambda w: w.name)
+def test_noalloc_scratch_serves_a_growing_batch(wl):
+    """Calls of 1, then all, then 2 sequences on the library's scratch: a call
+    with more (sequence, head) rows than the one before finds its arrival
+    counters at zero, not on that call's partials."""
+    print(f"[noalloc] growing batch {wl}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    if gpu.step_pairs is not None:
+        api.copy_blocks(gpu.cache, gpu.step_pairs)
+    k0, v0 = gpu.cache.k.clone(), gpu.cache.v.clone()
+    ref.append()
+    want = ref.decode()
+    for n in (1, wl.batch, 2):
+        args = (_sub(gpu.q, n), _sub(gpu.k_new, n), _sub(gpu.v_new, n), _sub(gpu.tables, n), _sub(gpu.ctx, n),
+                int(dr.ctx[:n].max()), gpu.sm_scale)
+        na = gpu.cache.with_pools(k0.clone(), v0.clone())
+        got = api.decode_step_noalloc(na, *args, out=torch.empty_like(args[0]))
+        fresh = api.decode_step(gpu.cache.with_pools(k0.clone(), v0.clone()), *args)
+        torch.cuda.synchronize()
+        assert torch.equal(got, fresh)
+        err = float(np.max(np.abs(out_f64(got) - want[:n])))
+        print(f"[noalloc] {wl.name}: batch {n}, max abs err {err:.3e}", flush=True)
+        assert err <= TOL[wl.kv]
