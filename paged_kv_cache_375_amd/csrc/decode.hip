@@ -455,8 +455,7 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
 // merge launch.  The workgroups run the per-head decode (head fastest, then
 // partition, then sequence, as decode_kernel), then, in the last prefix_wgs
 // of the grid, the prefix pass (the grouped kernel's body, one head tile of
-// 16 rows per workgroup, two waves; its grid linearised with the row sets
-// fastest).
+// 16 rows per workgroup, two waves, in the order described below).
 // Neither reads what the other writes: the prefix pass reads the groups'
 // shared blocks and q and writes workspace slots [0, pre); the decode reads
 // each sequence's own blocks past its shared tokens, writes slots from pre
