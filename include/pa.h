@@ -218,7 +218,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  * partials follow it.  Every completed call leaves its counters at zero, so
  * a workspace can be reused call after call with any sizes it is large
  * enough for (batches that grow and shrink included), provided every call on
- * it passes the same workspace_bytes.  Calls that overlap in time must not
+ * it passes the same workspace_bytes.  workspace_bytes is the size of the
+ * buffer itself and must not overstate it: the layout is derived from it.  Calls that overlap in time must not
  * share a workspace.  A context length of 0 yields zeros.  A
  * sequence whose context exceeds max_context_len or
  * max_blocks_per_seq * block_size, or whose table holds a block id outside
