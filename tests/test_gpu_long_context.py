@@ -3,8 +3,9 @@
 Contexts far past one launch's partitions exercise the merges at their
 largest: the per-head kernel's merge launch with more than 64 partials per
 head (its lanes then loop over the partials), the grouped kernel's in-launch
-merge over hundreds of partitions, and the longest context the library
-accepts (1024 partitions of 512 tokens).  Every output element is checked
+merge over hundreds of partitions, the shared-prefix path at long contexts,
+and the longest context the library accepts (1024 partitions of 512
+tokens).  Every output element is checked
 against the reference; the pool after the step is bit-exact."""
 import numpy as np
 import pytest
@@ -68,3 +69,34 @@ def test_context_past_the_limit_is_refused_before_any_launch():
     with pytest.raises(PagedAttnError) as e:
         api.decode(gpu.cache, gpu.q, gpu.tables, gpu.ctx, MAX_CONTEXT + 1, gpu.sm_scale)
     assert "max_context_len" in str(e.value)
+
+
+SHARED_CASES = {
+    # FP8 multi-head attention: the launch that holds the prefix pass and the
+    # per-head decode, then the merge launch over 2 prefix partials and 65 to
+    # 79 of the decode's per head
+    "shared_fp8_mha": Workload("long_sp_e4m3", 2, 2, 128, 16, 3, 33000, 40000, kv="e4m3", prefix_len=512),
+    # grouped decode (G 8) after a prefix pass of 4 partitions: the first
+    # partition starts from the prefix's state, hundreds merged in the launch
+    "shared_f16_gqa": Workload("long_sp_gqa", 16, 2, 128, 16, 2, 40000, 50000, prefix_len=1024),
+}
+
+
+@pytest.mark.parametrize("name", list(SHARED_CASES))
+def test_shared_prefix_long_context_parity(name):
+    wl = SHARED_CASES[name]
+    print(f"[long] {name}: building {wl}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    assert gpu.shared_blocks == wl.prefix_len // wl.block_size
+    out = out_f64(gpu.run(shared=True))
+    print(f"[long] {name}: reference", flush=True)
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    want = ref.decode()
+    err = float(np.max(np.abs(out - want)))
+    print(f"[long] {name}: contexts {dr.ctx.tolist()}, max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]
+    rel = 2e-3 if wl.kv != "e4m3" else 5e-3  # as for the unshared long contexts above
+    assert err <= rel * float(np.max(np.abs(want)))
