@@ -377,3 +377,12 @@ def test_shared_prefix_argument_checks_fail_before_any_launch():
     assert _shared(c, [0, 3], [19], mctx=1000, mb=64, wsb=need - 1) == _lib.PA_ERR_WORKSPACE_TOO_SMALL  # 304 tokens
     # no group shares anything: the plain decode's rules (f32 allowed)
     assert _shared(_cache(kv_dtype=_lib.PA_F32), [0, 0], [0], act=_lib.PA_F32, B=0) == _lib.PA_OK
+
+
+def test_timing_read_checks_its_arguments_and_holds_nothing_while_disabled():
+    L = _lib.lib()
+    assert L.pa_timing_enable(0) == _lib.PA_OK  # disabling creates and touches nothing
+    assert L.pa_timing_read(None, None) == _lib.PA_ERR_INVALID_ARGUMENT
+    ms, n = ctypes.c_double(1.0), ctypes.c_int32(7)
+    assert L.pa_timing_read(ctypes.byref(ms), ctypes.byref(n)) == _lib.PA_OK
+    assert (ms.value, n.value) == (0.0, 0)
