@@ -103,3 +103,47 @@ def test_noalloc_scratch_serves_a_growing_batch(wl):
         err = float(np.max(np.abs(out_f64(got) - want[:n])))
         print(f"[noalloc] {wl.name}: batch {n}, max abs err {err:.3e}", flush=True)
         assert err <= TOL[wl.kv]
+
+
+def test_noalloc_step_replays_from_a_hip_graph():
+    """The caller that cannot allocate, under HIP graph capture: a grouped
+    split-context step on the library's scratch is captured once and replayed
+    three times, with other GPU work between replays; every replay equals the
+    eager call bit for bit, and a larger eager call afterwards is still
+    correct (the counters each replay leaves are zero)."""
+    wl = CASES[0]  # grouped kernel (MQA), split contexts, arrival counters
+    print(f"[noalloc] graph {wl}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    k0, v0 = gpu.cache.k.clone(), gpu.cache.v.clone()
+    n = 2
+    args = (_sub(gpu.q, n), _sub(gpu.k_new, n), _sub(gpu.v_new, n), _sub(gpu.tables, n), _sub(gpu.ctx, n),
+            int(dr.ctx[:n].max()), gpu.sm_scale)
+    na = gpu.cache.with_pools(k0.clone(), v0.clone())
+    eager = api.decode_step_noalloc(na, *args, out=torch.empty_like(args[0])).clone()
+    out = torch.empty_like(args[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        api.decode_step_noalloc(na, *args, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        api.decode_step_noalloc(na, *args, out=out)
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(float("nan"))  # a fill kernel, outside the graph
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager call"
+        x = torch.randn(1 << 16, device="cuda")  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        del x
+    ref.append()
+    want = ref.decode()
+    assert float(np.max(np.abs(out_f64(out) - want[:n]))) <= TOL[wl.kv]
+    full = (gpu.q, gpu.k_new, gpu.v_new, gpu.tables, gpu.ctx, gpu.max_ctx, gpu.sm_scale)
+    got = api.decode_step_noalloc(gpu.cache.with_pools(k0.clone(), v0.clone()), *full, out=torch.empty_like(gpu.q))
+    err = float(np.max(np.abs(out_f64(got) - want)))
+    print(f"[noalloc] graph: replays bit-identical; then batch {wl.batch} eager, max abs err {err:.3e}", flush=True)
+    assert err <= TOL[wl.kv]
