@@ -83,6 +83,7 @@ struct Math;
 template <>
 struct Math<half_t, half_t> {  // f16 pool, f16 query: packed dot products
   static constexpr int EPL = 8;
+  static constexpr bool PAIRED = false;
   struct Q {
     uint32_t w[4];
   };
@@ -110,6 +111,7 @@ struct Math<half_t, half_t> {  // f16 pool, f16 query: packed dot products
 template <>
 struct Math<float, float> {  // f32 pool, f32 query
   static constexpr int EPL = 4;
+  static constexpr bool PAIRED = false;
   struct Q {
     float f[4];
   };
@@ -130,8 +132,10 @@ struct Math<float, float> {  // f32 pool, f32 query
 };
 
 template <>
-struct Math<fp8_t, half_t> {  // E4M3 pool, f16 query: K converted to f16 pairs (exact) for packed dots
+struct Math<fp8_t, half_t> {  // E4M3 pool, f16 query: K converted to f16 pairs (exact) for packed dots,
+                               // V accumulated two tokens at a time with f16 weights
   static constexpr int EPL = 16;
+  static constexpr bool PAIRED = true;
   struct Q {
     uint32_t w[8];  // the 16 query values as f16 pairs
   };
@@ -151,14 +155,27 @@ struct Math<fp8_t, half_t> {  // E4M3 pool, f16 query: K converted to f16 pairs 
     }
     return acc;
   }
-  static __device__ __forceinline__ void axpy(float* acc, const Vec16& v, float p) {
+  // acc[e] += p.x a[e] + p.y b[e] over the lane's 16 elements of two tokens'
+  // V rows a and b, the weights an f16 pair: each word's bytes of the two
+  // rows are interleaved (v_perm_b32: a0 b0 a1 b1, a2 b2 a3 b3), converted
+  // to f16 pairs (exact) and dotted with the weights (exact products, f32
+  // accumulation): 2.5 instructions per element pair instead of 3 for a
+  // conversion to f32 and two multiply-adds.  On FP8 pools the kernel's
+  // vector ALU is nearly saturated (a wave has a VALU instruction active in
+  // 27% of its cycles at three waves per SIMD), so this shows: FP8 prefix
+  // layer 98.5 -> 97.8 us, OPT-13B shape with an FP8 pool 66.2 -> 65.7 us.
+  static __device__ __forceinline__ void axpy2(float* acc, const Vec16& a, const Vec16& b, half2_t p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float2_t lo = e4m3x2_to_f32(v.w[i], false), hi = e4m3x2_to_f32(v.w[i], true);
-      acc[4 * i] += p * lo[0];
-      acc[4 * i + 1] += p * lo[1];
-      acc[4 * i + 2] += p * hi[0];
-      acc[4 * i + 3] += p * hi[1];
+      const uint32_t x01 = __builtin_amdgcn_perm(b.w[i], a.w[i], 0x05010400u);
+      const uint32_t x23 = __builtin_amdgcn_perm(b.w[i], a.w[i], 0x07030602u);
+      acc[4 * i] = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x01, 1.0f, false), p, acc[4 * i], false);
+      acc[4 * i + 1] =
+          __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x01, 1.0f, true), p, acc[4 * i + 1], false);
+      acc[4 * i + 2] =
+          __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x23, 1.0f, false), p, acc[4 * i + 2], false);
+      acc[4 * i + 3] =
+          __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x23, 1.0f, true), p, acc[4 * i + 3], false);
     }
   }
 };
@@ -166,6 +183,7 @@ struct Math<fp8_t, half_t> {  // E4M3 pool, f16 query: K converted to f16 pairs 
 template <>
 struct Math<fp8_t, float> {  // E4M3 pool, f32 query: exact hardware conversion to f32
   static constexpr int EPL = 16;
+  static constexpr bool PAIRED = false;
   struct Q {
     float f[16];
   };
@@ -377,11 +395,23 @@ __device__ __forceinline__ void decode_heads_body(const DecodeParams& P, const i
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+    if constexpr (M::PAIRED) {
+      // the weights of tokens u and u + 1 as an f16 pair; the sum takes the
+      // same rounded weights (a dot product with ones)
+      static_assert(U % 2 == 0, "tokens in pairs");
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float pu = exp2f(sc[u] - m_use);
-      l += pu;
-      M::axpy(acc, vr[u], pu);
+      for (int u = 0; u < U; u += 2) {
+        const half2_t p = __builtin_convertvector(float2_t{exp2f(sc[u] - m_use), exp2f(sc[u + 1] - m_use)}, half2_t);
+        l = __builtin_amdgcn_fdot2(p, half2_t{1, 1}, l, false);
+        M::axpy2(acc, vr[u], vr[u + 1], p);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float pu = exp2f(sc[u] - m_use);
+        l += pu;
+        M::axpy(acc, vr[u], pu);
+      }
     }
     m = m_new;
   }
