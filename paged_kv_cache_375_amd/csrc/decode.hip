@@ -499,10 +499,14 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(const DecodeParams P) {
 // with the prefix workgroups first in the grid and 106.1 with the prefix
 // pass as a launch of its own before the decode).  Both roles fit the
 // two-wave workgroup, and the prefix role's LDS leaves six workgroups per
-// CU, at which the FP8 decode runs no slower than at its own eight.
+// CU, at which the FP8 decode runs no slower than at its own eight.  Six
+// need three waves per SIMD, which the register budget is held to: left
+// free, the compiler gives the head_dim-128 instance 156 VGPRs and 40
+// accumulation registers, two waves per SIMD (FP8 prefix layer 98.1
+// against 98.5 us of launches, three runs each).
 template <int D>
-__global__ __launch_bounds__(2 * 64) void decode_prefix_fused_kernel(const DecodeParams P, int prefix_cols,
-                                                                      int prefix_wgs, int np) {
+__global__ __launch_bounds__(2 * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_prefix_fused_kernel(
+    const DecodeParams P, int prefix_cols, int prefix_wgs, int np) {
   static_assert(decode_waves<fp8_t>() == 2, "both roles use two-wave workgroups");
   const int i = blockIdx.x;
   const int ndec = static_cast<int>(gridDim.x) - prefix_wgs;
