@@ -44,7 +44,10 @@
  *
  * Supported shapes: head_dim in {32, 64, 128}; block_size a power of two in
  * 1..64; num_q_heads a multiple of num_kv_heads; kv dtype f32, f16 or
- * FP8 E4M3; activation dtype f32 or f16 (f32 only with an f32 pool).
+ * FP8 E4M3; activation dtype f16 (f16 or FP8 pool) or f32 (f32 or FP8
+ * pool).  Query heads sharing a KV head go to the matrix-core kernel only
+ * with f16 activations; with f32 ones every head is decoded on its own.
+ * Shared-prefix decode takes f16 activations only.
  * ---------------------------------------------------------------------------
  */
 #ifndef PA_H_

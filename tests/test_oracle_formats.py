@@ -79,3 +79,38 @@ def test_e4m3_quantise_matches_torch_on_all_f16_inputs(scale):
     big = x[finite][~inrange]
     got_big = np.array([oracle.e4m3_quantize(v, inv) for v in big.tolist()], dtype=np.uint8)
     assert np.all((got_big & 0x7F) == 0x7E)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.012345678])
+def test_e4m3_quantise_matches_torch_on_f32_inputs(scale):
+    """f32 activations: random binary32 bit patterns (every exponent) and the
+    binary32 neighbours of every rounding boundary, quantised with one
+    binary32 multiply by the inverse scale."""
+    inv = np.float32(1.0 / np.float64(np.float32(scale)))
+    x = f32_store_inputs(np.random.default_rng(7))
+    with np.errstate(over="ignore", invalid="ignore"):
+        x = (x * np.float32(scale)).astype(np.float32)  # the boundaries near where the scale puts them
+    finite = np.isfinite(x)
+    y = x[finite] * inv
+    inrange = np.abs(y) <= 448.0
+    ref = torch.from_numpy(y[inrange]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_quantize(v, inv) for v in x[finite][inrange].tolist()], dtype=np.uint8)
+    assert np.array_equal(got, ref)
+    got_big = np.array([oracle.e4m3_quantize(v, inv) for v in x[finite][~inrange].tolist()], dtype=np.uint8)
+    assert np.all((got_big & 0x7F) == 0x7E)
+
+
+def f32_store_inputs(rng, n_random=16384):
+    """binary32 inputs for the FP8 store: the neighbours (one ulp either side)
+    of every E4M3 value and of every midpoint between neighbouring values,
+    both signs; the saturation edge, infinities, NaN, zeros and binary32
+    subnormals; then random bit patterns."""
+    vals = np.array([oracle.e4m3_to_f64(c) for c in range(0x7F)], dtype=np.float32)
+    pts = list(vals) + [np.float32((vals[c] + vals[c + 1]) / 2) for c in range(0x7E)]
+    pts += [448.0, 464.0, 480.0, 1e30, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11, 1e-40]
+    pts = np.array(pts, dtype=np.float32)
+    pts = np.concatenate([pts, np.nextafter(pts, np.float32(np.inf)), np.nextafter(pts, np.float32(-np.inf))])
+    pts = np.concatenate([pts, -pts, np.array([np.inf, -np.inf, np.nan, 0.0, -0.0, np.finfo(np.float32).max],
+                                              dtype=np.float32)])
+    rand = rng.integers(0, 2 ** 32, size=n_random, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    return np.concatenate([pts.astype(np.float32), rand])
