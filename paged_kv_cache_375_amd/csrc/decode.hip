@@ -160,10 +160,11 @@ struct Math<fp8_t, half_t> {  // E4M3 pool, f16 query: K converted to f16 pairs 
   // rows are interleaved (v_perm_b32: a0 b0 a1 b1, a2 b2 a3 b3), converted
   // to f16 pairs (exact) and dotted with the weights (exact products, f32
   // accumulation): 2.5 instructions per element pair instead of 3 for a
-  // conversion to f32 and two multiply-adds.  On FP8 pools the kernel's
-  // vector ALU is nearly saturated (a wave has a VALU instruction active in
-  // 27% of its cycles at three waves per SIMD), so this shows: FP8 prefix
-  // layer 98.5 -> 97.8 us, OPT-13B shape with an FP8 pool 66.2 -> 65.7 us.
+  // conversion to f32 and two multiply-adds.  On FP8 pools the kernel does
+  // about twice the vector work per byte of f16 (a wave had a VALU
+  // instruction active in 27% of its cycles, at two waves per SIMD), so
+  // this shows: FP8 prefix layer 98.5 -> 97.8 us, OPT-13B shape with an FP8
+  // pool 66.2 -> 65.7 us.
   static __device__ __forceinline__ void axpy2(float* acc, const Vec16& a, const Vec16& b, half2_t p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
