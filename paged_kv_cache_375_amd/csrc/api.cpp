@@ -376,7 +376,7 @@ extern "C" pa_status pa_read_probe(const pa_kv_cache* cache, const int32_t* bloc
   if (mode == 0) {
     if (num_seqs < 0 || max_blocks_per_seq < 0 || max_context_len < 0)
       return fail(PA_ERR_INVALID_ARGUMENT, "%s: negative size", fn);
-    if (num_seqs > kMaxGridYZ || (max_context_len + 511) / 512 > kMaxGridYZ)
+    if (num_seqs > kMaxGridYZ || (max_context_len + pa::kPartitionTokens - 1) / pa::kPartitionTokens > kMaxGridYZ)
       return fail(PA_ERR_UNSUPPORTED, "%s: grid too large", fn);
     if (num_seqs > 0 && (!block_tables || !context_lens)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: NULL table", fn);
   }
