@@ -158,3 +158,43 @@ def test_random_shared_prefix_parity(i):
     print(f"[shared-prefix] {wl.name}: max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
     assert np.all(np.isfinite(out))
     assert err <= TOL[wl.kv]
+
+
+def random_fused_case(i):
+    """FP8 multi-head attention with blocks of at least 16 tokens and at least
+    one wave load's tokens: the prefix pass runs inside the per-head decode's
+    launch.  Random head size, block size, head count, prefix (on or inside a
+    block), lengths, up to five groups (some empty) with random claims, and
+    sequences outside every group at both ends."""
+    rng = np.random.default_rng(3000 + i)
+    d = int(rng.choice([32, 64, 128]))
+    bs = int(rng.choice([b for b in (16, 32, 64) if b >= 64 // (d // 16)]))
+    h = int(rng.choice([1, 3, 8, 17, 40]))
+    prefix = int(rng.integers(1, 1200 // bs + 1)) * bs + int(rng.integers(0, 2)) * int(rng.integers(1, bs))
+    hi = int(rng.integers(1, 1501))
+    lo = int(rng.integers(1, hi + 1))
+    b = int(rng.integers(2, max(3, min(48, int(1.5e6 // (h * (prefix + (lo + hi) / 2))))) + 1))
+    wl = Workload(f"spfused{i}_h{h}_d{d}_bs{bs}_B{b}_p{prefix}_ctx{lo}-{hi}", h, h, d, bs, b, lo, hi, kv="e4m3",
+                  prefix_len=prefix)
+    k = int(rng.integers(1, 6))
+    starts = sorted(int(x) for x in rng.integers(0, b + 1, size=k + 1))
+    claims = [int(rng.integers(0, prefix // bs + 1)) for _ in range(k)]
+    return wl, starts, claims, bool(i % 2 == 0)
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_fused_shared_prefix_parity(i):
+    wl, starts, claims, fused = random_fused_case(i)
+    print(f"[shared-prefix] {wl.name} groups {starts} claims {claims} fused={fused}", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    t = gpu.scenario.tables
+    for g in range(len(claims)):
+        assert (t[starts[g]:starts[g + 1], :claims[g]] == t[starts[g], :claims[g]]).all()
+    out = out_f64(_run(gpu, starts, claims, fused))
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    err = float(np.max(np.abs(out - ref.decode_threaded())))
+    print(f"[shared-prefix] {wl.name}: max abs err {err:.3e} (bound {TOL[wl.kv]})", flush=True)
+    assert np.all(np.isfinite(out))
+    assert err <= TOL[wl.kv]
