@@ -172,6 +172,23 @@ def test_full_workload_parity(name):
     full_size_check(name, wl, out, ref, dr)
 
 
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 32, 64])
+def test_full_mqa_block_size_sweep(bs):
+    """The Falcon-7B MQA layer at its real size at every other block size of
+    the sweep (16 is the workload itself, above): the same lengths and K/V
+    values, placement re-drawn.  Blocks below 16 tokens take the grouped
+    kernel's per-row addressing.  Pool bit-exact, every output element
+    within the bound."""
+    wl = WORKLOADS["falcon7b_mqa"].with_block_size(bs)
+    print(f"[full] {wl.name}: building", flush=True)
+    dr, gpu, ref = build_pair(wl)
+    out = out_f64(gpu.run())
+    ref.append()
+    assert np.array_equal(pool_bytes(gpu.cache.k), ref.k.view(np.uint8))
+    assert np.array_equal(pool_bytes(gpu.cache.v), ref.v.view(np.uint8))
+    full_size_check(wl.name, wl, out, ref, dr)
+
+
 @pytest.mark.parametrize("scale", [-0.0883883, 0.0, 0.35], ids=["negative", "zero", "large"])
 @pytest.mark.parametrize("case", [(71, 1, 64, "f16", 16), (64, 8, 128, "e4m3", 16), (16, 16, 128, "f16", 16)],
                          ids=["mqa_grouped", "gqa_fp8_grouped", "mha_per_head"])
