@@ -153,7 +153,10 @@ def test_group_kernel_special_cases(hq, hkv, d):
     assert torch.count_nonzero(out0) == 0
 
 
-FULL = ["opt13b", "llama70b_gqa", "falcon7b_mqa", "opt13b_fp8_prefix", "llama70b_gqa_tp8", "opt13b_tp8"]
+# opt13b_fp8_prefix505: the 505-token prefix ends inside a block, so every
+# sequence's first write copies that shared block first (64 copies)
+FULL = ["opt13b", "llama70b_gqa", "falcon7b_mqa", "opt13b_fp8_prefix", "opt13b_fp8_prefix505", "llama70b_gqa_tp8",
+        "opt13b_tp8"]
 
 
 @pytest.mark.parametrize("name", FULL)
