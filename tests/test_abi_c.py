@@ -1,9 +1,9 @@
-"""The public header as C, and the library's behaviour when host memory runs
+"""The public header as C and C++, and the library's behaviour when host memory runs
 out (CPU only, no kernel launches).
 
-* include/pa.h compiles as strict C99 (gcc -std=c99 -pedantic -Werror); the
-  program links against the built library and drives the allocator through
-  a fork and a copy-on-write [F55 §常见问题]; [IPX §同一提示生成两个回答的假想例子].
+* include/pa.h compiles as strict C99 (gcc -std=c99 -pedantic -Werror) and
+  as C++17; the program links against the built library and drives the
+  allocator through a fork and a copy-on-write [F55 §常见问题]; [IPX §同一提示生成两个回答的假想例子].
 * A host allocation that fails inside an entry point returns
   PA_ERR_HOST_MEMORY and changes nothing: checked in a child process whose
   address space is capped just above what it already uses.
@@ -57,6 +57,24 @@ def test_header_is_c99_and_links(tmp_path):
     src.write_text(C_PROGRAM)
     exe = tmp_path / "use_pa"
     cmd = ["gcc", "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", f"-I{os.path.join(ROOT, 'include')}",
+           str(src), f"-L{LIBDIR}", "-lpagedattn", f"-Wl,-rpath,{LIBDIR}", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "C99 OK PA_ERR_HOST_MEMORY" in r.stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_header_is_cpp_and_links(tmp_path):
+    """The same program as C++17 (the header's declarations are noexcept
+    there and linked with C names)."""
+    lib = os.path.join(LIBDIR, "libpagedattn.so")
+    assert os.path.exists(lib), "build the library first"
+    src = tmp_path / "use_pa.cpp"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "use_pa_cpp"
+    cmd = ["g++", "-std=c++17", "-pedantic", "-Wall", "-Wextra", "-Werror", f"-I{os.path.join(ROOT, 'include')}",
            str(src), f"-L{LIBDIR}", "-lpagedattn", f"-Wl,-rpath,{LIBDIR}", "-o", str(exe)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
